@@ -1,0 +1,202 @@
+/*
+ * i8gs.h -- C ABI of the group-scaled INT8 linear layer for AMD MI355X (gfx950).
+ *
+ * The operation (sources are web pages, cited by title and section):
+ *  - "Flint-DFlash2-GPTQ-INT8-PTQR" model card, format table: GPTQ checkpoint
+ *    (qweight / qzeros / scales, no g_idx, desc_act false), INT8 weights served
+ *    W8A8, group size 128, symmetric; format audit: every matrix uses contiguous
+ *    groups of exactly 128 weights; serving notes: the W8A8 GEMM path quantises
+ *    its bf16 inputs to INT8 on the fly (rounding mode "round").
+ *  - "Qwen3.8-27B GPTQ INT8 W8A8 GS128 PTQR" model card, "Quantization details":
+ *    true int8 x int8 compute at every decode and prefill shape, with one weight
+ *    scale per 128-wide K block.
+ *  - "Qwen3.8-27B-DFlash2-W4A16-g128-sym-GPTQ" model card, property table: the
+ *    4-bit weight-only sibling (W4A16, group_size 128, symmetric); dequant-patch
+ *    table: INT32-packed GPTQ is unpacked from int32 and scaled per group.
+ *  - "Qwen3.5-4B-DFlash-W8A16" model card: RTN weight quantisation with no
+ *    calibration data; recovering dense weight rows through the layer itself.
+ *
+ *  For an activation row x[m, 0..K) (bf16) and packed weights:
+ *    a_scale[m] = max_k |x[m,k]| / 127                         (fp32, IEEE division)
+ *    qa[m,k]    = clamp(round_half_even(x[m,k] / a_scale[m]), -127, 127)   (int8;
+ *                 an all-zero row gives a_scale 0 and codes 0)
+ *    q[k,n]     = code(k,n) - 2^(bits-1)      (GPTQ offset binary, bits = 8 or 4)
+ *    P[m,g,n]   = sum_{k = 128g}^{128g+127} qa[m,k] * q[k,n]   (exact int32)
+ *    y[m,n]     = bf16( a_scale[m] * sum_g w_scale[g,n] * P[m,g,n] )
+ *  The group sums are exact; the fold over groups is fp32 in any order, so y is
+ *  within one bf16 unit of the exact value plus (K/128 + 2) * 2^-24 times
+ *  a_scale[m] * sum_g |w_scale[g,n] * P[m,g,n]|.
+ *
+ * Layouts (all row-major, little-endian):
+ *  x        bf16   [M, ldx]        activations (ldx >= K, ldx % 8 == 0)
+ *  qa       int8   [M, K]          quantised activations
+ *  a_scale  fp32   [M]
+ *  qweight  int32  [K / (32/bits), N]  code j of word [r, n] is k = (32/bits)*r + j,
+ *                                  stored in bits [bits*j, bits*j + bits) of the word
+ *  w_scale  fp32   [K/128, N]      one scale per 128-wide K group per column
+ *  y        bf16   [M, ldy]        (ldy >= N, ldy % 8 == 0)
+ *  qzeros is not taken: symmetric checkpoints store the constant mid-range code.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or retains memory and never synchronises the stream.
+ *    Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) of the
+ *    current HIP device.  Calls are reentrant.
+ *  - Return value: I8GS_OK or an i8gs_status code.  Every argument is validated
+ *    before anything is launched; on a validation error nothing is launched and
+ *    nothing is written.  i8gs_last_error() then returns a message (thread-local)
+ *    that names the violated rule.  Unsupported requests are rejected explicitly;
+ *    there is no fallback path.
+ *  - Shapes: K % 128 == 0 and K > 0 for the GEMMs; N % 8 == 0; M >= 0 (M == 0
+ *    or N == 0 is a no-op that returns I8GS_OK).  Tensor pointers must be 16-byte
+ *    aligned.  Dimensions must be below 2^31.
+ *  - The device must be gfx950 (I8GS_ERR_UNSUPPORTED_DEVICE otherwise).
+ */
+#ifndef I8GS_H
+#define I8GS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define I8GS_ABI_VERSION 1
+
+typedef enum {
+    I8GS_OK = 0,
+    I8GS_ERR_INVALID_ARG = 1,       /* null pointer, bad enum, x and qa both / neither given */
+    I8GS_ERR_UNSUPPORTED_SHAPE = 2, /* K % 128, N % 8, negative or too large sizes, ld < dim */
+    I8GS_ERR_MISALIGNED = 3,        /* a tensor pointer is not 16-byte aligned */
+    I8GS_ERR_WORKSPACE = 4,         /* workspace missing or smaller than i8gs_workspace_bytes() */
+    I8GS_ERR_HIP = 5,               /* a HIP runtime call or kernel launch failed */
+    I8GS_ERR_UNSUPPORTED_DEVICE = 6 /* current device is not gfx950 */
+} i8gs_status;
+
+/* Operation ids for i8gs_workspace_bytes(). */
+#define I8GS_OP_W8A8 0
+#define I8GS_OP_W4A16 1
+
+/* Kernel choice for gemm_w8a8_g128_ex(). */
+#define I8GS_KERNEL_AUTO 0   /* decode kernel for M <= 64, tiled kernel otherwise */
+#define I8GS_KERNEL_DECODE 1 /* weight-streaming kernel (M <= 64 only) */
+#define I8GS_KERNEL_TILED 2  /* LDS-tiled MFMA kernel, any M */
+
+/* ABI version of the loaded library (I8GS_ABI_VERSION at build time). */
+int i8gs_abi_version(void);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char *i8gs_last_error(void);
+
+/* Name of a status code, e.g. "I8GS_ERR_UNSUPPORTED_SHAPE". */
+const char *i8gs_status_string(int status);
+
+/*
+ * Dynamic per-token INT8 activation quantisation (Flint card serving notes;
+ * Qwen3.8-27B W8A8 card serving section).  For each of the M rows of x:
+ * a_scale[m] = absmax/127 in fp32 and qa[m,:] = clamp(rint(x / a_scale), -127, 127)
+ * with a correctly rounded fp32 division and ties to even.
+ *   x        device bf16 [M, ldx], K % 8 == 0, ldx >= K, ldx % 8 == 0
+ *   qa       device int8 [M, K] (contiguous), output
+ *   a_scale  device fp32 [M], output
+ * Results are bit-exact (one correct value per element).
+ */
+int quant_act_per_token(const void *x, int64_t ldx, int64_t M, int64_t K, int8_t *qa,
+                        float *a_scale, void *stream);
+
+/*
+ * Bytes of workspace gemm_w8a8_g128 (op I8GS_OP_W8A8) or gemm_w4a16_g128
+ * (I8GS_OP_W4A16) needs for these sizes.  Layout: a fixed 64 KiB region of
+ * split-K arrival counters at offset 0, then (W8A8) the quantised activations used
+ * when x is passed (M*K bytes + 4*M, each piece rounded up to 256 bytes; always
+ * counted), then the split-K partial sums.  Returns 0 when no workspace is needed
+ * (W4A16 without a K split) and (size_t)-1 for invalid arguments.
+ *
+ * Workspace contract: the counter region must be zero when a call starts, and
+ * every completed call leaves it zero again, whatever the shape.  Zero-fill a
+ * newly allocated workspace once before its first use; after that it can be
+ * reused by calls of any shape.  Do not share one workspace between calls that
+ * may run concurrently (different streams without ordering).
+ */
+size_t i8gs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
+
+/* Same, for gemm_w8a8_g128_ex() with an explicit kernel / split-K choice. */
+size_t i8gs_workspace_bytes_ex(int op, int64_t M, int64_t N, int64_t K, int kernel, int split_k);
+
+/*
+ * W8A8 G128 linear (Qwen3.8-27B W8A8 card "Quantization details"; Flint card
+ * format table and serving notes):  y = bf16(a_scale * sum_g w_scale[g] * P_g).
+ * Pass EITHER x (bf16 [M, ldx]; it is quantised per token into the workspace
+ * first) OR the pre-quantised pair qa (int8 [M, K]) and a_scale (fp32 [M]);
+ * the others must be NULL.  qweight is int32 [K/4, N] with 8-bit codes q + 128;
+ * w_scale fp32 [K/128, N]; y bf16 [M, ldy].  workspace: device memory of at
+ * least i8gs_workspace_bytes(I8GS_OP_W8A8, M, N, K) bytes (may be NULL if that
+ * is 0).  Output y is within the tolerance stated at the top of this file.
+ */
+int gemm_w8a8_g128(const void *x, int64_t ldx, const int8_t *qa, const float *a_scale,
+                   const int32_t *qweight, const float *w_scale, void *y, int64_t ldy, int64_t M,
+                   int64_t N, int64_t K, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gemm_w8a8_g128 with the kernel chosen by the caller: kernel is one of
+ * I8GS_KERNEL_*; split_k (decode kernel only) is the number of workgroups that
+ * share one column tile's K range, 0 for the automatic choice (it is clamped to
+ * K/128).  Every choice computes the same exact group sums; only the fp32 fold
+ * order differs.  I8GS_KERNEL_DECODE with M > 64 is rejected.
+ */
+int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float *a_scale,
+                      const int32_t *qweight, const float *w_scale, void *y, int64_t ldy, int64_t M,
+                      int64_t N, int64_t K, int kernel, int split_k, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
+ * The per-group int32 partials P[m, g, n] = sum_{k in group g} qa[m,k] * q[k,n]
+ * of the W8A8 G128 GEMM, written to P (device int32 [M, K/128, N]) instead of
+ * being folded.  Same block code as gemm_w8a8_g128; used to check the integer
+ * stage bit-exactly.
+ */
+int gemm_w8a8_g128_group_partials(const int8_t *qa, const int32_t *qweight, int32_t *P,
+                                  int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * W4A16 g128 weight-only linear (Qwen3.8-27B-DFlash2 W4A16 card, property and
+ * quantised-layer tables): y[m,n] = bf16( sum_g w_scale[g,n] * sum_{k in g} x[m,k]*q[k,n] )
+ * with q = nibble - 8 in [-8, 7].  x bf16 [M, ldx]; qweight int32 [K/8, N] (nibble j of
+ * word [r, n] is k = 8r + j); w_scale fp32 [K/128, N]; y bf16 [M, ldy].  Weights are
+ * dequantised in registers to exact integer-valued bf16, each group is summed by bf16
+ * MFMA in fp32 and then scaled, so y is within one bf16 unit of the exact value plus
+ * (K/128 + 130) * 2^-24 * sum_g |w_scale| * sum_k |x*q|.
+ * workspace: i8gs_workspace_bytes(I8GS_OP_W4A16, M, N, K) bytes (may be NULL if 0).
+ */
+int gemm_w4a16_g128(const void *x, int64_t ldx, const int32_t *qweight, const float *w_scale,
+                    void *y, int64_t ldy, int64_t M, int64_t N, int64_t K, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
+ * GPTQ unpack (W4A16 card dequant-patch table, "unpack from int32 plus group
+ * scales"; the W8A16 card's identity probe recovers the same dense rows).
+ * From qweight int32 [K/(32/bits), N] (bits = 8 or 4) write, for each output that is
+ * not NULL:  q_out int8 [K, N] = code - 2^(bits-1);  w_out fp32 [K, N] =
+ * fl32(w_scale[k/128, n] * q[k, n]) (w_scale required when w_out is given).
+ * At least one output must be given.  Bit-exact.
+ */
+int gptq_unpack(const int32_t *qweight, const float *w_scale, int bits, int64_t K, int64_t N,
+                int8_t *q_out, float *w_out, void *stream);
+
+/*
+ * Round-to-nearest G128 symmetric weight quantisation with GPTQ packing (W4A16
+ * card scripts: RTN with no calibration data; W8A16 card: pure RTN).  From w fp32
+ * [K, N]: w_scale[g, n] = absmax over the group / qmax (fp32; qmax = 127 for 8 bits,
+ * 7 for 4 bits), q = clamp(rint(w / w_scale), -127, 127) or (-8, 7) (q = 0 when
+ * the group is all zero), written as codes q + 2^(bits-1) into qweight int32
+ * [K/(32/bits), N].  K % 128 == 0.  Bit-exact.
+ */
+int gptq_quantize_rtn(const float *w, int bits, int64_t K, int64_t N, int32_t *qweight,
+                      float *w_scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* I8GS_H */

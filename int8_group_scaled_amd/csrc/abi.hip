@@ -1,0 +1,297 @@
+// C ABI entry points of libi8gs: argument validation, workspace sizing, dispatch.
+// Validation is pure host logic and happens before any HIP call, so a rejected
+// call launches nothing and writes nothing.
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace i8gs {
+
+static thread_local std::string g_last_error;
+
+int fail(int status, const std::string &msg) {
+    g_last_error = std::string(i8gs_status_string(status)) + ": " + msg;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return I8GS_OK;
+}
+
+int hip_check(hipError_t e, const char *what) {
+    if (e == hipSuccess) return I8GS_OK;
+    return fail(I8GS_ERR_HIP, std::string(what) + " failed: " + hipGetErrorString(e));
+}
+
+int check_device() {
+    static std::mutex mu;
+    static std::vector<int> verdict;  // per device: 0 unknown, 1 ok, 2 bad
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_check(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)verdict.size() <= dev) verdict.resize(dev + 1, 0);
+    if (verdict[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_check(e, "hipGetDeviceProperties");
+        verdict[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (verdict[dev] == 2)
+            return fail(I8GS_ERR_UNSUPPORTED_DEVICE,
+                        std::string("device is ") + prop.gcnArchName + "; only gfx950 (MI355X) is supported");
+    }
+    if (verdict[dev] == 2) return fail(I8GS_ERR_UNSUPPORTED_DEVICE, "only gfx950 (MI355X) is supported");
+    return I8GS_OK;
+}
+
+}  // namespace i8gs
+
+using namespace i8gs;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+std::string fmt(const char *f, long long a, long long b = 0, long long c = 0) {
+    char buf[256];
+    snprintf(buf, sizeof buf, f, a, b, c);
+    return buf;
+}
+
+int check_dims(int64_t M, int64_t N, int64_t K, bool need_group) {
+    if (M < 0 || N < 0 || K < 0)
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("sizes must be >= 0 (M=%lld N=%lld K=%lld)", M, N, K));
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "sizes must be below 2^31");
+    if (need_group && (K == 0 || K % kGroup != 0))
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE,
+                    fmt("K=%lld must be a positive multiple of the 128-wide weight group", K));
+    if (N % 8 != 0) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("N=%lld must be a multiple of 8", N));
+    return I8GS_OK;
+}
+
+int check_ptr(const void *p, const char *name) {
+    if (!p) return fail(I8GS_ERR_INVALID_ARG, std::string(name) + " is NULL");
+    if (!aligned16(p)) return fail(I8GS_ERR_MISALIGNED, std::string(name) + " is not 16-byte aligned");
+    return I8GS_OK;
+}
+
+int check_ld(int64_t ld, int64_t dim, const char *name) {
+    if (ld < dim || ld % 8 != 0 || ld > kMaxDim)
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE,
+                    std::string(name) + fmt("=%lld must be >= %lld and a multiple of 8", ld, dim));
+    return I8GS_OK;
+}
+
+size_t w8a8_quant_bytes(int64_t M, int64_t K) { return align256(size_t(M) * size_t(K)) + align256(size_t(M) * 4); }
+
+}  // namespace
+
+#define I8GS_TRY(expr)              \
+    do {                            \
+        int _rc = (expr);           \
+        if (_rc != I8GS_OK) return _rc; \
+    } while (0)
+
+extern "C" {
+
+int i8gs_abi_version(void) { return I8GS_ABI_VERSION; }
+
+const char *i8gs_last_error(void) { return g_last_error.c_str(); }
+
+const char *i8gs_status_string(int status) {
+    switch (status) {
+        case I8GS_OK: return "I8GS_OK";
+        case I8GS_ERR_INVALID_ARG: return "I8GS_ERR_INVALID_ARG";
+        case I8GS_ERR_UNSUPPORTED_SHAPE: return "I8GS_ERR_UNSUPPORTED_SHAPE";
+        case I8GS_ERR_MISALIGNED: return "I8GS_ERR_MISALIGNED";
+        case I8GS_ERR_WORKSPACE: return "I8GS_ERR_WORKSPACE";
+        case I8GS_ERR_HIP: return "I8GS_ERR_HIP";
+        case I8GS_ERR_UNSUPPORTED_DEVICE: return "I8GS_ERR_UNSUPPORTED_DEVICE";
+        default: return "I8GS_ERR_UNKNOWN";
+    }
+}
+
+int quant_act_per_token(const void *x, int64_t ldx, int64_t M, int64_t K, int8_t *qa,
+                        float *a_scale, void *stream) {
+    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim)
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("sizes must be in [0, 2^31) (M=%lld K=%lld)", M, K));
+    if (K % 8 != 0) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("K=%lld must be a multiple of 8", K));
+    if (M == 0) return ok();
+    if (K == 0) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "K must be positive when M > 0");
+    I8GS_TRY(check_ptr(x, "x"));
+    I8GS_TRY(check_ptr(qa, "qa"));
+    I8GS_TRY(check_ptr(a_scale, "a_scale"));
+    I8GS_TRY(check_ld(ldx, K, "ldx"));
+    if (int64_t(M) * ldx > (int64_t(1) << 40)) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "x too large");
+    I8GS_TRY(check_device());
+    I8GS_TRY(hip_check(launch_quant_act((const uint16_t *)x, ldx, (int)M, (int)K, qa, a_scale,
+                                        (hipStream_t)stream),
+                       "quant_act_per_token launch"));
+    return ok();
+}
+
+size_t i8gs_workspace_bytes_ex(int op, int64_t M, int64_t N, int64_t K, int kernel, int split_k) {
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return (size_t)-1;
+    if (op == I8GS_OP_W8A8) {
+        if (kernel < I8GS_KERNEL_AUTO || kernel > I8GS_KERNEL_TILED || split_k < 0) return (size_t)-1;
+        if (M == 0 || N == 0) return 0;
+        if (K == 0 || K % kGroup != 0) return (size_t)-1;
+        return kCounterBytes + w8a8_quant_bytes(M, K) + w8a8_gemm_workspace((int)M, (int)N, (int)K, kernel, split_k);
+    }
+    if (op == I8GS_OP_W4A16) {
+        if (M == 0 || N == 0) return 0;
+        if (K == 0 || K % kGroup != 0) return (size_t)-1;
+        const size_t part = w4a16_gemm_workspace((int)M, (int)N, (int)K);
+        return part ? kCounterBytes + part : 0;
+    }
+    return (size_t)-1;
+}
+
+size_t i8gs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
+    return i8gs_workspace_bytes_ex(op, M, N, K, I8GS_KERNEL_AUTO, 0);
+}
+
+int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float *a_scale,
+                      const int32_t *qweight, const float *w_scale, void *y, int64_t ldy, int64_t M,
+                      int64_t N, int64_t K, int kernel, int split_k, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    I8GS_TRY(check_dims(M, N, K, true));
+    if (kernel < I8GS_KERNEL_AUTO || kernel > I8GS_KERNEL_TILED)
+        return fail(I8GS_ERR_INVALID_ARG, fmt("kernel=%lld is not one of I8GS_KERNEL_*", kernel));
+    if (split_k < 0) return fail(I8GS_ERR_INVALID_ARG, fmt("split_k=%lld must be >= 0", split_k));
+    if (kernel == I8GS_KERNEL_DECODE && M > 64)
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("the decode kernel takes M <= 64 (M=%lld)", M));
+    const bool have_x = x != nullptr;
+    const bool have_q = qa != nullptr || a_scale != nullptr;
+    if (have_x == have_q)
+        return fail(I8GS_ERR_INVALID_ARG,
+                    "pass either x (bf16 activations) or the pre-quantised pair qa/a_scale, not both or neither");
+    if (M == 0 || N == 0) return ok();
+    if (have_x) {
+        I8GS_TRY(check_ptr(x, "x"));
+        I8GS_TRY(check_ld(ldx, K, "ldx"));
+    } else {
+        I8GS_TRY(check_ptr(qa, "qa"));
+        I8GS_TRY(check_ptr(a_scale, "a_scale"));
+    }
+    I8GS_TRY(check_ptr(qweight, "qweight"));
+    I8GS_TRY(check_ptr(w_scale, "w_scale"));
+    I8GS_TRY(check_ptr(y, "y"));
+    I8GS_TRY(check_ld(ldy, N, "ldy"));
+    const size_t gemm_ws = w8a8_gemm_workspace((int)M, (int)N, (int)K, kernel, split_k);
+    const size_t qbytes = w8a8_quant_bytes(M, K);
+    const size_t need = kCounterBytes + qbytes + gemm_ws;
+    if (have_x || gemm_ws > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(I8GS_ERR_WORKSPACE, fmt("workspace of %lld bytes needed, %lld given", (long long)need,
+                                                 workspace ? (long long)workspace_bytes : 0LL));
+        if (!aligned16(workspace)) return fail(I8GS_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    }
+    I8GS_TRY(check_device());
+    hipStream_t s = (hipStream_t)stream;
+    char *wsp = (char *)workspace;
+    if (have_x) {
+        int8_t *qa_ws = (int8_t *)(wsp + kCounterBytes);
+        float *as_ws = (float *)(wsp + kCounterBytes + align256(size_t(M) * size_t(K)));
+        I8GS_TRY(hip_check(launch_quant_act((const uint16_t *)x, ldx, (int)M, (int)K, qa_ws, as_ws, s),
+                           "quant_act_per_token launch"));
+        qa = qa_ws;
+        a_scale = as_ws;
+    }
+    W8A8Args a{qa, a_scale, qweight, w_scale, (uint16_t *)y, ldy, nullptr, (int)M, (int)N, (int)K, kernel, split_k,
+               gemm_ws ? (int *)wsp : nullptr, gemm_ws ? (void *)(wsp + kCounterBytes + qbytes) : nullptr, gemm_ws};
+    I8GS_TRY(hip_check(launch_w8a8_gemm(a, s), "gemm_w8a8_g128 launch"));
+    return ok();
+}
+
+int gemm_w8a8_g128(const void *x, int64_t ldx, const int8_t *qa, const float *a_scale,
+                   const int32_t *qweight, const float *w_scale, void *y, int64_t ldy, int64_t M,
+                   int64_t N, int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
+    return gemm_w8a8_g128_ex(x, ldx, qa, a_scale, qweight, w_scale, y, ldy, M, N, K, I8GS_KERNEL_AUTO, 0,
+                             workspace, workspace_bytes, stream);
+}
+
+int gemm_w8a8_g128_group_partials(const int8_t *qa, const int32_t *qweight, int32_t *P,
+                                  int64_t M, int64_t N, int64_t K, void *stream) {
+    I8GS_TRY(check_dims(M, N, K, true));
+    if (M == 0 || N == 0) return ok();
+    I8GS_TRY(check_ptr(qa, "qa"));
+    I8GS_TRY(check_ptr(qweight, "qweight"));
+    I8GS_TRY(check_ptr(P, "P"));
+    I8GS_TRY(check_device());
+    W8A8Args a{qa, nullptr, qweight, nullptr, nullptr, 0, P, (int)M, (int)N, (int)K, I8GS_KERNEL_TILED, 0,
+               nullptr, nullptr, 0};
+    I8GS_TRY(hip_check(launch_w8a8_gemm(a, (hipStream_t)stream), "group partials launch"));
+    return ok();
+}
+
+int gemm_w4a16_g128(const void *x, int64_t ldx, const int32_t *qweight, const float *w_scale,
+                    void *y, int64_t ldy, int64_t M, int64_t N, int64_t K, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    I8GS_TRY(check_dims(M, N, K, true));
+    if (M == 0 || N == 0) return ok();
+    I8GS_TRY(check_ptr(x, "x"));
+    I8GS_TRY(check_ld(ldx, K, "ldx"));
+    I8GS_TRY(check_ptr(qweight, "qweight"));
+    I8GS_TRY(check_ptr(w_scale, "w_scale"));
+    I8GS_TRY(check_ptr(y, "y"));
+    I8GS_TRY(check_ld(ldy, N, "ldy"));
+    const size_t part = w4a16_gemm_workspace((int)M, (int)N, (int)K);
+    const size_t need = part ? kCounterBytes + part : 0;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(I8GS_ERR_WORKSPACE, fmt("workspace of %lld bytes needed, %lld given", (long long)need,
+                                                 workspace ? (long long)workspace_bytes : 0LL));
+        if (!aligned16(workspace)) return fail(I8GS_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    }
+    I8GS_TRY(check_device());
+    char *wsp = (char *)workspace;
+    W4A16Args a{(const uint16_t *)x, ldx, qweight, w_scale, (uint16_t *)y, ldy, (int)M, (int)N, (int)K,
+                part ? (int *)wsp : nullptr, part ? (void *)(wsp + kCounterBytes) : nullptr, part};
+    I8GS_TRY(hip_check(launch_w4a16_gemm(a, (hipStream_t)stream), "gemm_w4a16_g128 launch"));
+    return ok();
+}
+
+int gptq_unpack(const int32_t *qweight, const float *w_scale, int bits, int64_t K, int64_t N,
+                int8_t *q_out, float *w_out, void *stream) {
+    if (bits != 4 && bits != 8) return fail(I8GS_ERR_INVALID_ARG, fmt("bits=%lld must be 4 or 8", bits));
+    I8GS_TRY(check_dims(0, N, K, true));
+    if (!q_out && !w_out) return fail(I8GS_ERR_INVALID_ARG, "give q_out, w_out or both");
+    if (N == 0) return ok();
+    I8GS_TRY(check_ptr(qweight, "qweight"));
+    if (q_out) I8GS_TRY(check_ptr(q_out, "q_out"));
+    if (w_out) {
+        I8GS_TRY(check_ptr(w_out, "w_out"));
+        I8GS_TRY(check_ptr(w_scale, "w_scale"));
+    }
+    I8GS_TRY(check_device());
+    I8GS_TRY(hip_check(launch_gptq_unpack(qweight, w_scale, bits, (int)K, (int)N, q_out, w_out,
+                                          (hipStream_t)stream),
+                       "gptq_unpack launch"));
+    return ok();
+}
+
+int gptq_quantize_rtn(const float *w, int bits, int64_t K, int64_t N, int32_t *qweight,
+                      float *w_scale, void *stream) {
+    if (bits != 4 && bits != 8) return fail(I8GS_ERR_INVALID_ARG, fmt("bits=%lld must be 4 or 8", bits));
+    I8GS_TRY(check_dims(0, N, K, true));
+    if (N == 0) return ok();
+    I8GS_TRY(check_ptr(w, "w"));
+    I8GS_TRY(check_ptr(qweight, "qweight"));
+    I8GS_TRY(check_ptr(w_scale, "w_scale"));
+    I8GS_TRY(check_device());
+    I8GS_TRY(hip_check(launch_gptq_rtn(w, bits, (int)K, (int)N, qweight, w_scale, (hipStream_t)stream),
+                       "gptq_quantize_rtn launch"));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Internal declarations shared by the HIP translation units of libi8gs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "i8gs.h"
+
+namespace i8gs {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kGroup = 128;
+
+// Records a message for i8gs_last_error() and returns `status`.
+int fail(int status, const std::string &msg);
+// Clears the thread's last error and returns I8GS_OK.
+int ok();
+// Checks a HIP call result; on failure records it and returns I8GS_ERR_HIP.
+int hip_check(hipError_t e, const char *what);
+// Checks that the current device is gfx950 (cached per device).
+int check_device();
+
+// Kernel launchers (no validation; callers validate first).
+hipError_t launch_quant_act(const uint16_t *x, int64_t ldx, int M, int K, int8_t *qa,
+                            float *a_scale, hipStream_t s);
+hipError_t launch_gptq_unpack(const int32_t *qw, const float *ws, int bits, int K, int N,
+                              int8_t *q_out, float *w_out, hipStream_t s);
+hipError_t launch_gptq_rtn(const float *w, int bits, int K, int N, int32_t *qw, float *ws,
+                           hipStream_t s);
+
+struct W8A8Args {
+    const int8_t *qa;
+    const float *a_scale;
+    const int32_t *qweight;
+    const float *w_scale;
+    uint16_t *y;
+    int64_t ldy;
+    int32_t *P;  // non-null: write group partials instead of y
+    int M, N, K;
+    int kernel;   // I8GS_KERNEL_*
+    int split_k;  // 0 = automatic
+    int *counters;  // split-K arrival counters (kMaxCounters, zero on entry)
+    void *ws;       // split-K partial sums
+    size_t ws_bytes;
+};
+size_t w8a8_gemm_workspace(int M, int N, int K, int kernel, int split_k);
+hipError_t launch_w8a8_gemm(const W8A8Args &a, hipStream_t s);
+
+struct W4A16Args {
+    const uint16_t *x;
+    int64_t ldx;
+    const int32_t *qweight;
+    const float *w_scale;
+    uint16_t *y;
+    int64_t ldy;
+    int M, N, K;
+    int *counters;
+    void *ws;
+    size_t ws_bytes;
+};
+size_t w4a16_gemm_workspace(int M, int N, int K);
+hipError_t launch_w4a16_gemm(const W4A16Args &a, hipStream_t s);
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round an fp32 value to bfloat16, nearest with ties to even.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0;  // NaN
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Every GEMM workspace starts with this many bytes of split-K arrival counters.
+// The region sits at the same offset whatever the shape, so a caller can reuse one
+// zero-filled workspace across calls of different shapes: each call leaves the
+// counters it used at zero.
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr int kMaxCounters = int(kCounterBytes / sizeof(int));
+
+}  // namespace i8gs

@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/i8gs.h declares, and rejects invalid arguments before
+touching the device (each rejection is a pure host decision)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "i8gs.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import int8_group_scaled_amd as i8
+    return i8.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_binding_exports():
+    import int8_group_scaled_amd as i8
+    assert _declared_functions() == sorted(i8.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    path = os.path.join(ROOT, "int8_group_scaled_amd", "libi8gs.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_abi_version_and_strings(lib):
+    import int8_group_scaled_amd as i8
+    assert i8.abi_version() == 1
+    assert lib.i8gs_status_string(2) == b"I8GS_ERR_UNSUPPORTED_SHAPE"
+    assert lib.i8gs_status_string(99) == b"I8GS_ERR_UNKNOWN"
+
+
+# A 16-byte aligned host buffer stands in for device pointers: every call below is
+# rejected during validation, before any pointer is dereferenced or HIP is called.
+_buf = (ctypes.c_uint8 * 4096)()
+_base = (ctypes.addressof(_buf) + 15) & ~15
+A = ctypes.c_void_p(_base)
+MIS = ctypes.c_void_p(_base + 4)
+NUL = None
+
+
+def _w8a8(lib, x=A, ldx=512, qa=NUL, a_s=NUL, qw=A, ws=A, y=A, ldy=256, M=8, N=256, K=512, kernel=0, split=0,
+          work=A, wbytes=1 << 30):
+    return lib.gemm_w8a8_g128_ex(x, ldx, qa, a_s, qw, ws, y, ldy, M, N, K, kernel, split, work, wbytes, NUL)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(K=500, ldx=504), 2, "multiple of the 128-wide"),
+    (dict(K=0, ldx=0), 2, "multiple of the 128-wide"),
+    (dict(N=250, ldy=256), 2, "multiple of 8"),
+    (dict(M=-1), 2, ">= 0"),
+    (dict(M=1 << 31), 2, "below 2^31"),
+    (dict(ldx=500), 2, "ldx"),
+    (dict(ldy=128), 2, "ldy"),
+    (dict(qa=A, a_s=A), 1, "not both or neither"),
+    (dict(x=NUL), 1, "not both or neither"),
+    (dict(qw=NUL), 1, "qweight is NULL"),
+    (dict(ws=NUL), 1, "w_scale is NULL"),
+    (dict(y=MIS), 3, "y is not 16-byte aligned"),
+    (dict(x=MIS), 3, "x is not 16-byte aligned"),
+    (dict(work=NUL), 4, "workspace"),
+    (dict(wbytes=16), 4, "workspace"),
+    (dict(kernel=7), 1, "I8GS_KERNEL"),
+    (dict(split=-2), 1, "split_k"),
+    (dict(kernel=1, M=65), 2, "decode kernel"),
+])
+def test_w8a8_validation(lib, kwargs, status, needle):
+    rc = _w8a8(lib, **kwargs)
+    assert rc == status
+    msg = lib.i8gs_last_error().decode()
+    assert needle in msg, msg
+
+
+def test_empty_inputs_are_noops(lib):
+    assert _w8a8(lib, M=0) == 0
+    assert _w8a8(lib, N=0, ldy=0) == 0
+    assert lib.quant_act_per_token(A, 512, 0, 512, A, A, NUL) == 0
+    assert lib.gemm_w4a16_g128(A, 512, A, A, A, 256, 0, 256, 512, NUL, 0, NUL) == 0
+
+
+def test_quant_validation(lib):
+    assert lib.quant_act_per_token(A, 512, 4, 500, A, A, NUL) == 2
+    assert lib.quant_act_per_token(A, 504, 4, 512, A, A, NUL) == 2
+    assert lib.quant_act_per_token(NUL, 512, 4, 512, A, A, NUL) == 1
+    assert lib.quant_act_per_token(A, 512, 4, 512, MIS, A, NUL) == 3
+    assert lib.quant_act_per_token(A, 512, 4, 0, A, A, NUL) == 2
+
+
+def test_w4a16_and_utility_validation(lib):
+    assert lib.gemm_w4a16_g128(A, 512, A, A, A, 256, 8, 256, 384 + 64, A, 1 << 30, NUL) == 2
+    assert lib.gemm_w4a16_g128(A, 512, NUL, A, A, 256, 8, 256, 512, A, 1 << 30, NUL) == 1
+    assert lib.gptq_unpack(A, A, 5, 512, 256, A, NUL, NUL) == 1
+    assert lib.gptq_unpack(A, A, 8, 512, 256, NUL, NUL, NUL) == 1
+    assert lib.gptq_unpack(A, NUL, 8, 512, 256, NUL, A, NUL) == 1
+    assert lib.gptq_unpack(A, A, 4, 200, 256, A, NUL, NUL) == 2
+    assert lib.gptq_quantize_rtn(A, 3, 512, 256, A, A, NUL) == 1
+    assert lib.gptq_quantize_rtn(A, 8, 512, 12, A, A, NUL) == 2
+    assert lib.gemm_w8a8_g128_group_partials(A, A, NUL, 8, 256, 512, NUL) == 1
+
+
+def test_workspace_sizes(lib):
+    import int8_group_scaled_amd as i8
+    # 64 KiB of counters, then the quantised activations (M*K + 4*M, each rounded to 256 bytes)
+    assert i8.workspace_bytes(i8.OP_W8A8, 8, 256, 512, i8.KERNEL_TILED) == 65536 + 4096 + 256
+    assert i8.workspace_bytes(i8.OP_W8A8, 0, 256, 512) == 0
+    with pytest.raises(ValueError):
+        i8.workspace_bytes(i8.OP_W8A8, 8, 256, 500)
+    with pytest.raises(ValueError):
+        i8.workspace_bytes(7, 8, 256, 512)
+    # a decode split adds counters and partial tiles
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 6144, 5120, i8.KERNEL_DECODE, 3) > 64 * 5120

@@ -1,0 +1,158 @@
+"""GPU parity of the W8A8 G128 GEMM: per-group int32 partials bit-exact, bf16
+outputs within the tolerance in parity.py, on the workloads' layer shapes (in
+the launch configuration the benchmark times) and on ragged edge cases."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import int8_group_scaled_amd as i8
+import oracle
+import synth
+from parity import assert_within_tolerance, dev, dev_bf16, host_bf16_bits, rtn_weights, unpacked
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, tag, M, K, N, outliers):
+    xb = synth.activations_bf16(seed, tag, M, K, outliers)
+    qw, ws = rtn_weights(seed, tag, K, N, 8)
+    return xb, qw, ws
+
+
+@pytest.mark.parametrize("M,K,N", [(8, 512, 256), (64, 5120, 6144), (100, 384, 72), (1, 128, 8)])
+def test_group_partials_bit_exact(M, K, N):
+    xb, qw, _ = _case(0, f"p{M}-{K}-{N}", M, K, N, True)
+    qa, _ = oracle.quant_act_per_token(xb)
+    P = i8.gemm_w8a8_g128_group_partials(dev(qa), dev(qw))
+    torch.cuda.synchronize()
+    assert np.array_equal(P.cpu().numpy(), oracle.group_partials(qa, oracle.gptq_unpack(qw, 8, K)))
+
+
+def test_group_partials_full_code_range():
+    """Uniformly random codes (all 256, including q = -128) and random activation codes."""
+    M, K, N = 48, 1024, 96
+    words = synth.uniform_words(5, "pcodes", (K // 4) * N).reshape(K // 4, N)
+    qa = (synth.uniform_words(5, "pqa", M * K // 4).view(np.uint8).reshape(M, K).astype(np.int16) - 128)
+    qa = np.clip(qa, -127, 127).astype(np.int8)
+    P = i8.gemm_w8a8_g128_group_partials(dev(qa), dev(words))
+    torch.cuda.synchronize()
+    assert np.array_equal(P.cpu().numpy(), oracle.group_partials(qa, oracle.gptq_unpack(words, 8, K)))
+
+
+@pytest.mark.parametrize("layer", ["qkv", "o_proj", "gate_up", "down"])
+def test_decode_layer(layer):
+    """Decode workload: 64 tokens through each drafter linear, full output, from bf16 x."""
+    L = synth.LAYERS[layer]
+    M = 64
+    xb, qw, ws = _case(0, f"decode-{layer}", M, L.K, L.N, True)
+    y = i8.gemm_w8a8_g128(dev(qw), dev(ws), x=dev_bf16(xb))
+    torch.cuda.synchronize()
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, unpacked(0, f"decode-{layer}", L.K, L.N, 8), ws)
+    beyond, maxulp = assert_within_tolerance(host_bf16_bits(y), y_exact, T, L.K, what=f"decode {layer}")
+    print(f"decode {layer}: {beyond} of {y_exact.size} beyond a bare ulp, max {maxulp:.3f} ulp")
+
+
+def test_single_linear_both_modes():
+    M, K, N = 8, 512, 256
+    xb, qw, ws = _case(0, "single", M, K, N, False)
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, oracle.gptq_unpack(qw, 8, K), ws)
+    y1 = i8.gemm_w8a8_g128(dev(qw), dev(ws), x=dev_bf16(xb))
+    y2 = i8.gemm_w8a8_g128(dev(qw), dev(ws), qa=dev(qa), a_scale=dev(s))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16_bits(y1), host_bf16_bits(y2))
+    assert_within_tolerance(host_bf16_bits(y1), y_exact, T, K, what="single")
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 128, 8), (17, 384, 40), (63, 1024, 264), (64, 256, 520), (65, 640, 136), (100, 1152, 200), (3, 17408, 64),
+])
+def test_ragged_shapes(M, K, N):
+    xb, qw, ws = _case(1, f"rag{M}-{K}-{N}", M, K, N, True)
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, oracle.gptq_unpack(qw, 8, K), ws)
+    y = i8.gemm_w8a8_g128(dev(qw), dev(ws), x=dev_bf16(xb))
+    torch.cuda.synchronize()
+    assert_within_tolerance(host_bf16_bits(y), y_exact, T, K, what=f"ragged {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 7, 40])
+def test_decode_split_k_variants(split):
+    """Every split count gives an in-tolerance result, and repeating a call is bitwise identical."""
+    M, K, N = 64, 5120, 512
+    xb, qw, ws = _case(2, "splits", M, K, N, True)
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, oracle.gptq_unpack(qw, 8, K), ws)
+    args = (dev(qw), dev(ws))
+    ya = i8.gemm_w8a8_g128_ex(*args, x=dev_bf16(xb), kernel=i8.KERNEL_DECODE, split_k=split)
+    yb = i8.gemm_w8a8_g128_ex(*args, x=dev_bf16(xb), kernel=i8.KERNEL_DECODE, split_k=split)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16_bits(ya), host_bf16_bits(yb))
+    assert_within_tolerance(host_bf16_bits(ya), y_exact, T, K, what=f"split {split}")
+
+
+def test_decode_and_tiled_kernels_agree_with_oracle():
+    M, K, N = 64, 2048, 384
+    xb, qw, ws = _case(3, "kernels", M, K, N, True)
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, oracle.gptq_unpack(qw, 8, K), ws)
+    for kern in (i8.KERNEL_DECODE, i8.KERNEL_TILED):
+        y = i8.gemm_w8a8_g128_ex(dev(qw), dev(ws), qa=dev(qa), a_scale=dev(s), kernel=kern)
+        torch.cuda.synchronize()
+        assert_within_tolerance(host_bf16_bits(y), y_exact, T, K, what=f"kernel {kern}")
+
+
+def test_identity_probe_recovers_dequantised_rows():
+    """Running an identity matrix through the layer returns the dense dequantised
+    weight rows (the W8A8-W8A16 drafter card's identity probe): row m is e_m, so
+    a_scale = fl(1/127), qa = 127 e_m, and y[m, :] = bf16(fl(1/127) * 127 * w_scale * q)."""
+    K, N = 512, 256
+    _, qw, ws = _case(4, "probe", 8, K, N, False)
+    eye = synth.bf16_bits_from_f32(np.eye(K, dtype=np.float32))
+    y = i8.gemm_w8a8_g128(dev(qw), dev(ws), x=dev_bf16(eye))
+    _, w = i8.gptq_unpack(dev(qw), 8, dev(ws), want_codes=False, want_dequant=True)
+    torch.cuda.synchronize()
+    qa, s = oracle.quant_act_per_token(eye)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, oracle.gptq_unpack(qw, 8, K), ws)
+    yb = host_bf16_bits(y)
+    assert_within_tolerance(yb, y_exact, T, K, what="identity probe")
+    dense = synth.bf16_bits_from_f32(w.cpu().numpy())
+    # the probe and the unpacked rows agree to within one bf16 unit
+    diff = np.abs(synth.f32_from_bf16_bits(yb).astype(np.float64) - synth.f32_from_bf16_bits(dense))
+    from parity import ulp_bf16
+    assert np.all(diff <= ulp_bf16(w.cpu().numpy().astype(np.float64)))
+
+
+@pytest.mark.parametrize("layer", ["qkv", "o_proj", "gate_up", "down", "fc"])
+def test_prefill_layer_sampled_rows(layer):
+    """Prefill workload (4096 tokens): full GPU output, 24 sampled rows checked (incl. first and last)."""
+    L = synth.LAYERS[layer]
+    M = 4096
+    xb, qw, ws = _case(0, f"prefill-{layer}", M, L.K, L.N, True)
+    y = i8.gemm_w8a8_g128(dev(qw), dev(ws), x=dev_bf16(xb))
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(0, f"prefill-{layer}", M, 24)
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, unpacked(0, f"prefill-{layer}", L.K, L.N, 8), ws, rows=rows)
+    yb = host_bf16_bits(y)[rows]
+    assert_within_tolerance(yb, y_exact, T, L.K, what=f"prefill {layer}")
+    # integer stage of the same rows, bit-exact
+    P = i8.gemm_w8a8_g128_group_partials(dev(qa[rows]), dev(qw))
+    torch.cuda.synchronize()
+    assert np.array_equal(P.cpu().numpy(), oracle.group_partials(qa[rows], unpacked(0, f"prefill-{layer}", L.K, L.N, 8)))
+
+
+def test_lm_head_sampled_rows():
+    """INT8 vocabulary head: 64 tokens x 248320 columns; 6 sampled rows checked against the oracle."""
+    L = synth.LAYERS["lm_head"]
+    M = 64
+    xb, qw, ws = _case(0, "lm_head", M, L.K, L.N, False)
+    y = i8.gemm_w8a8_g128(dev(qw), dev(ws), x=dev_bf16(xb))
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(0, "lm_head", M, 6)
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, unpacked(0, "lm_head", L.K, L.N, 8), ws, rows=rows)
+    assert_within_tolerance(host_bf16_bits(y)[rows], y_exact, T, L.K, what="lm_head")
