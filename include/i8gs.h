@@ -49,7 +49,7 @@
  *    there is no fallback path.
  *  - Shapes: K % 128 == 0 and K > 0 for the GEMMs; N % 8 == 0; M >= 0 (M == 0
  *    or N == 0 is a no-op that returns I8GS_OK).  Tensor pointers must be 16-byte
- *    aligned.  Dimensions must be below 2^31.
+ *    aligned.  Dimensions must be below 2^31, and K*N and M*K below 2^32.
  *  - The device must be gfx950 (I8GS_ERR_UNSUPPORTED_DEVICE otherwise).
  */
 #ifndef I8GS_H
@@ -121,8 +121,8 @@ int quant_act_per_token(const void *x, int64_t ldx, int64_t M, int64_t K, int8_t
  */
 size_t i8gs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 
-/* Same, for gemm_w8a8_g128_ex() with an explicit kernel / split-K choice. */
-size_t i8gs_workspace_bytes_ex(int op, int64_t M, int64_t N, int64_t K, int kernel, int split_k);
+/* Same, for gemm_w8a8_g128_ex() with an explicit kernel / workgroup-count choice. */
+size_t i8gs_workspace_bytes_ex(int op, int64_t M, int64_t N, int64_t K, int kernel, int decode_workgroups);
 
 /*
  * W8A8 G128 linear (Qwen3.8-27B W8A8 card "Quantization details"; Flint card
@@ -140,14 +140,15 @@ int gemm_w8a8_g128(const void *x, int64_t ldx, const int8_t *qa, const float *a_
 
 /*
  * gemm_w8a8_g128 with the kernel chosen by the caller: kernel is one of
- * I8GS_KERNEL_*; split_k (decode kernel only) is the number of workgroups that
- * share one column tile's K range, 0 for the automatic choice (it is clamped to
- * K/128).  Every choice computes the same exact group sums; only the fp32 fold
- * order differs.  I8GS_KERNEL_DECODE with M > 64 is rejected.
+ * I8GS_KERNEL_*; decode_workgroups (decode kernel only) is the number of
+ * workgroups that share the (64-column tile x 128-wide K group) work items
+ * evenly, 0 for the automatic choice (one per compute unit); it is clamped to the
+ * number of work items.  Every choice computes the same exact group sums; only
+ * the fp32 fold order differs.  I8GS_KERNEL_DECODE with M > 64 is rejected.
  */
 int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float *a_scale,
                       const int32_t *qweight, const float *w_scale, void *y, int64_t ldy, int64_t M,
-                      int64_t N, int64_t K, int kernel, int split_k, void *workspace,
+                      int64_t N, int64_t K, int kernel, int decode_workgroups, void *workspace,
                       size_t workspace_bytes, void *stream);
 
 /*

@@ -139,10 +139,11 @@ def _workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
     return ws
 
 
-def workspace_bytes(op: int, M: int, N: int, K: int, kernel: int = KERNEL_AUTO, split_k: int = 0) -> int:
-    n = load_library().i8gs_workspace_bytes_ex(op, M, N, K, kernel, split_k)
+def workspace_bytes(op: int, M: int, N: int, K: int, kernel: int = KERNEL_AUTO, decode_workgroups: int = 0) -> int:
+    n = load_library().i8gs_workspace_bytes_ex(op, M, N, K, kernel, decode_workgroups)
     if n == ctypes.c_size_t(-1).value:
-        raise ValueError(f"invalid workspace query op={op} M={M} N={N} K={K} kernel={kernel} split_k={split_k}")
+        raise ValueError(f"invalid workspace query op={op} M={M} N={N} K={K} kernel={kernel} "
+                         f"decode_workgroups={decode_workgroups}")
     return int(n)
 
 
@@ -167,7 +168,8 @@ def quant_act_per_token(x: torch.Tensor, qa: Optional[torch.Tensor] = None,
 
 def gemm_w8a8_g128_ex(qweight: torch.Tensor, w_scale: torch.Tensor, x: Optional[torch.Tensor] = None,
                       qa: Optional[torch.Tensor] = None, a_scale: Optional[torch.Tensor] = None,
-                      y: Optional[torch.Tensor] = None, kernel: int = KERNEL_AUTO, split_k: int = 0) -> torch.Tensor:
+                      y: Optional[torch.Tensor] = None, kernel: int = KERNEL_AUTO,
+                      decode_workgroups: int = 0) -> torch.Tensor:
     """W8A8 G128 linear from bf16 x [M, K] or from (qa, a_scale); qweight int32 [K/4, N],
     w_scale fp32 [K/128, N] -> y bf16 [M, N]."""
     _need(qweight, "qweight", torch.int32, 2)
@@ -201,10 +203,10 @@ def gemm_w8a8_g128_ex(qweight: torch.Tensor, w_scale: torch.Tensor, x: Optional[
     _need(y, "y", torch.bfloat16, 2)
     if tuple(y.shape) != (M, N):
         raise ValueError(f"y must be [{M}, {N}]")
-    nbytes = workspace_bytes(OP_W8A8, M, N, K, kernel, split_k) if x is not None or M > 0 else 0
+    nbytes = workspace_bytes(OP_W8A8, M, N, K, kernel, decode_workgroups)
     ws = _workspace(dev, nbytes)
     _raise(load_library().gemm_w8a8_g128_ex(_ptr(x), ldx, _ptr(qa), _ptr(a_scale), _ptr(qweight), _ptr(w_scale),
-                                            _ptr(y), y.stride(0), M, N, K, kernel, split_k, _ptr(ws),
+                                            _ptr(y), y.stride(0), M, N, K, kernel, decode_workgroups, _ptr(ws),
                                             0 if ws is None else ws.numel(), _stream(dev)))
     return y
 

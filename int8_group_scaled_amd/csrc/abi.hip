@@ -75,6 +75,10 @@ int check_dims(int64_t M, int64_t N, int64_t K, bool need_group) {
         return fail(I8GS_ERR_UNSUPPORTED_SHAPE,
                     fmt("K=%lld must be a positive multiple of the 128-wide weight group", K));
     if (N % 8 != 0) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("N=%lld must be a multiple of 8", N));
+    // one layer's 8-bit weights (K*N bytes) and activations (M*K) must stay below 4 GiB
+    // (32-bit buffer offsets in the kernels)
+    if (K * N >= (int64_t(1) << 32) || M * K >= (int64_t(1) << 32))
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "K*N and M*K must be below 2^32");
     return I8GS_OK;
 }
 
@@ -139,13 +143,14 @@ int quant_act_per_token(const void *x, int64_t ldx, int64_t M, int64_t K, int8_t
     return ok();
 }
 
-size_t i8gs_workspace_bytes_ex(int op, int64_t M, int64_t N, int64_t K, int kernel, int split_k) {
+size_t i8gs_workspace_bytes_ex(int op, int64_t M, int64_t N, int64_t K, int kernel, int decode_workgroups) {
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return (size_t)-1;
     if (op == I8GS_OP_W8A8) {
-        if (kernel < I8GS_KERNEL_AUTO || kernel > I8GS_KERNEL_TILED || split_k < 0) return (size_t)-1;
+        if (kernel < I8GS_KERNEL_AUTO || kernel > I8GS_KERNEL_TILED || decode_workgroups < 0) return (size_t)-1;
         if (M == 0 || N == 0) return 0;
         if (K == 0 || K % kGroup != 0) return (size_t)-1;
-        return kCounterBytes + w8a8_quant_bytes(M, K) + w8a8_gemm_workspace((int)M, (int)N, (int)K, kernel, split_k);
+        return kCounterBytes + w8a8_quant_bytes(M, K) +
+               w8a8_gemm_workspace((int)M, (int)N, (int)K, kernel, decode_workgroups);
     }
     if (op == I8GS_OP_W4A16) {
         if (M == 0 || N == 0) return 0;
@@ -162,12 +167,13 @@ size_t i8gs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
 
 int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float *a_scale,
                       const int32_t *qweight, const float *w_scale, void *y, int64_t ldy, int64_t M,
-                      int64_t N, int64_t K, int kernel, int split_k, void *workspace,
+                      int64_t N, int64_t K, int kernel, int decode_workgroups, void *workspace,
                       size_t workspace_bytes, void *stream) {
     I8GS_TRY(check_dims(M, N, K, true));
     if (kernel < I8GS_KERNEL_AUTO || kernel > I8GS_KERNEL_TILED)
         return fail(I8GS_ERR_INVALID_ARG, fmt("kernel=%lld is not one of I8GS_KERNEL_*", kernel));
-    if (split_k < 0) return fail(I8GS_ERR_INVALID_ARG, fmt("split_k=%lld must be >= 0", split_k));
+    if (decode_workgroups < 0)
+        return fail(I8GS_ERR_INVALID_ARG, fmt("decode_workgroups=%lld must be >= 0", decode_workgroups));
     if (kernel == I8GS_KERNEL_DECODE && M > 64)
         return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("the decode kernel takes M <= 64 (M=%lld)", M));
     const bool have_x = x != nullptr;
@@ -187,7 +193,7 @@ int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float 
     I8GS_TRY(check_ptr(w_scale, "w_scale"));
     I8GS_TRY(check_ptr(y, "y"));
     I8GS_TRY(check_ld(ldy, N, "ldy"));
-    const size_t gemm_ws = w8a8_gemm_workspace((int)M, (int)N, (int)K, kernel, split_k);
+    const size_t gemm_ws = w8a8_gemm_workspace((int)M, (int)N, (int)K, kernel, decode_workgroups);
     const size_t qbytes = w8a8_quant_bytes(M, K);
     const size_t need = kCounterBytes + qbytes + gemm_ws;
     if (have_x || gemm_ws > 0) {
@@ -207,7 +213,8 @@ int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float 
         qa = qa_ws;
         a_scale = as_ws;
     }
-    W8A8Args a{qa, a_scale, qweight, w_scale, (uint16_t *)y, ldy, nullptr, (int)M, (int)N, (int)K, kernel, split_k,
+    W8A8Args a{qa, a_scale, qweight, w_scale, (uint16_t *)y, ldy, nullptr, (int)M, (int)N, (int)K, kernel,
+               decode_workgroups,
                gemm_ws ? (int *)wsp : nullptr, gemm_ws ? (void *)(wsp + kCounterBytes + qbytes) : nullptr, gemm_ws};
     I8GS_TRY(hip_check(launch_w8a8_gemm(a, s), "gemm_w8a8_g128 launch"));
     return ok();

@@ -44,12 +44,12 @@ struct W8A8Args {
     int32_t *P;  // non-null: write group partials instead of y
     int M, N, K;
     int kernel;   // I8GS_KERNEL_*
-    int split_k;  // 0 = automatic
+    int workgroups;  // decode kernel workgroups, 0 = automatic
     int *counters;  // split-K arrival counters (kMaxCounters, zero on entry)
     void *ws;       // split-K partial sums
     size_t ws_bytes;
 };
-size_t w8a8_gemm_workspace(int M, int N, int K, int kernel, int split_k);
+size_t w8a8_gemm_workspace(int M, int N, int K, int kernel, int workgroups);
 hipError_t launch_w8a8_gemm(const W8A8Args &a, hipStream_t s);
 
 struct W4A16Args {

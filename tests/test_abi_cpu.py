@@ -79,7 +79,7 @@ def _w8a8(lib, x=A, ldx=512, qa=NUL, a_s=NUL, qw=A, ws=A, y=A, ldy=256, M=8, N=2
     (dict(work=NUL), 4, "workspace"),
     (dict(wbytes=16), 4, "workspace"),
     (dict(kernel=7), 1, "I8GS_KERNEL"),
-    (dict(split=-2), 1, "split_k"),
+    (dict(split=-2), 1, "decode_workgroups"),
     (dict(kernel=1, M=65), 2, "decode kernel"),
 ])
 def test_w8a8_validation(lib, kwargs, status, needle):
@@ -125,5 +125,5 @@ def test_workspace_sizes(lib):
         i8.workspace_bytes(i8.OP_W8A8, 8, 256, 500)
     with pytest.raises(ValueError):
         i8.workspace_bytes(7, 8, 256, 512)
-    # a decode split adds counters and partial tiles
-    assert i8.workspace_bytes(i8.OP_W8A8, 64, 6144, 5120, i8.KERNEL_DECODE, 3) > 64 * 5120
+    # the decode kernel adds two partial tiles per workgroup
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 6144, 5120, i8.KERNEL_DECODE, 3) > 65536 + 64 * 5120 + 3 * 2 * 16384

@@ -79,19 +79,19 @@ def test_ragged_shapes(M, K, N):
     assert_within_tolerance(host_bf16_bits(y), y_exact, T, K, what=f"ragged {M}x{K}x{N}")
 
 
-@pytest.mark.parametrize("split", [1, 2, 3, 7, 40])
-def test_decode_split_k_variants(split):
-    """Every split count gives an in-tolerance result, and repeating a call is bitwise identical."""
+@pytest.mark.parametrize("wgs", [1, 2, 3, 7, 40, 97, 256, 10000])
+def test_decode_workgroup_counts(wgs):
+    """Every stream-K grid size gives an in-tolerance result, and repeating a call is bitwise identical."""
     M, K, N = 64, 5120, 512
     xb, qw, ws = _case(2, "splits", M, K, N, True)
     qa, s = oracle.quant_act_per_token(xb)
     y_exact, T = oracle.gemm_w8a8_g128(qa, s, oracle.gptq_unpack(qw, 8, K), ws)
     args = (dev(qw), dev(ws))
-    ya = i8.gemm_w8a8_g128_ex(*args, x=dev_bf16(xb), kernel=i8.KERNEL_DECODE, split_k=split)
-    yb = i8.gemm_w8a8_g128_ex(*args, x=dev_bf16(xb), kernel=i8.KERNEL_DECODE, split_k=split)
+    ya = i8.gemm_w8a8_g128_ex(*args, x=dev_bf16(xb), kernel=i8.KERNEL_DECODE, decode_workgroups=wgs)
+    yb = i8.gemm_w8a8_g128_ex(*args, x=dev_bf16(xb), kernel=i8.KERNEL_DECODE, decode_workgroups=wgs)
     torch.cuda.synchronize()
     assert np.array_equal(host_bf16_bits(ya), host_bf16_bits(yb))
-    assert_within_tolerance(host_bf16_bits(ya), y_exact, T, K, what=f"split {split}")
+    assert_within_tolerance(host_bf16_bits(ya), y_exact, T, K, what=f"{wgs} workgroups")
 
 
 def test_decode_and_tiled_kernels_agree_with_oracle():
