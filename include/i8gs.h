@@ -141,10 +141,12 @@ int gemm_w8a8_g128(const void *x, int64_t ldx, const int8_t *qa, const float *a_
 /*
  * gemm_w8a8_g128 with the kernel chosen by the caller: kernel is one of
  * I8GS_KERNEL_*; decode_workgroups (decode kernel only) is the number of
- * workgroups that share the (64-column tile x 128-wide K group) work items
+ * workgroups that share the (128-column tile x 128-wide K group) work items
  * evenly, 0 for the automatic choice (one per compute unit); it is clamped to the
  * number of work items.  Every choice computes the same exact group sums; only
- * the fp32 fold order differs.  I8GS_KERNEL_DECODE with M > 64 is rejected.
+ * the fp32 fold order differs.  I8GS_KERNEL_DECODE is rejected when M > 64 or
+ * when M*ldy*2 >= 2^31 (32-bit output offsets); I8GS_KERNEL_AUTO takes the tiled
+ * kernel in that case.
  */
 int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float *a_scale,
                       const int32_t *qweight, const float *w_scale, void *y, int64_t ldy, int64_t M,

@@ -193,6 +193,9 @@ int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float 
     I8GS_TRY(check_ptr(w_scale, "w_scale"));
     I8GS_TRY(check_ptr(y, "y"));
     I8GS_TRY(check_ld(ldy, N, "ldy"));
+    if (kernel == I8GS_KERNEL_DECODE && !decode_y_fits(M, ldy))
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE,
+                    fmt("the decode kernel needs M*ldy*2 < 2^31 bytes of y (M=%lld ldy=%lld)", M, ldy));
     const size_t gemm_ws = w8a8_gemm_workspace((int)M, (int)N, (int)K, kernel, decode_workgroups);
     const size_t qbytes = w8a8_quant_bytes(M, K);
     const size_t need = kCounterBytes + qbytes + gemm_ws;

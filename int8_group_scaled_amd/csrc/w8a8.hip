@@ -18,16 +18,10 @@
 // two's-complement int8 value of q.
 //
 // Two kernels:
-//  * decode (M <= 64): bound by streaming the weights from HBM.  A workgroup owns a
-//    tile of 64 columns and a range of K groups; its W waves split that range, and
-//    every wave loads its weights straight from HBM into registers as 16-byte row
-//    pieces (one wave instruction = 256 contiguous bytes of 4 rows) and its
-//    activation fragments from L2, with the next group's loads in flight while the
-//    current group runs on the MFMA units.  Waves reduce through LDS in a fixed
-//    order.  When the tiles alone cannot fill the GPU, K is also split across S
-//    workgroups: each writes an fp32 partial tile to the workspace, and the last of
-//    the S to arrive (a per-tile atomic counter) sums the partials in split order
-//    and writes y, so results do not depend on timing.
+//  * decode (M <= 64): bound by streaming the weights from HBM.  One workgroup per
+//    CU streams an equal share of (tile, group) units through an LDS ring filled by
+//    direct buffer-to-LDS copies; tiles split between workgroups are summed in a
+//    fixed order by a small reduction kernel.
 //  * tiled (M > 64): LDS-staged 128x128 tiles, four waves of 64x64.
 #include "internal.h"
 
@@ -38,9 +32,9 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Workgroup barrier that orders only LDS: waits for this wave's LDS accesses, not for
-// its global loads (the fence of __syncthreads would drain the prefetches too).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Workgroup barrier without the fence of __syncthreads (which would also wait for
+// every copy in flight); the compiler keeps memory accesses on their side of it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ v4i flip(v4i v) {
     return v ^ (int)0x80808080;
@@ -48,336 +42,316 @@ __device__ __forceinline__ v4i flip(v4i v) {
 
 // ------------------------------------------------------------------ decode kernel
 //
-// Weight operand.  A 64-column slab is read as 16-byte row pieces: lane (li, lb) =
-// (lane % 16, lane / 16) owns the four adjacent columns c = n0 + 4*li .. +3 and, for
-// the 64-wide K step s of group g, loads rows 32g + 16s + 4*lb + i (i = 0..3) of
-// those columns; one wave instruction reads 256 contiguous bytes of 4 rows.  For
-// column c + cc the four words are 16 consecutive K bytes (k = 128g + 64s + 16*lb ..
-// +15): exactly the B operand of lane (li, lb) of an MFMA whose 16 columns are
-// n0 + 4*j + cc.  So a slab is 4 MFMA fragments with column stride 4 and no data
-// moves between lanes; fragment cc's result in lane (li, lb) is column
-// n0 + 4*li + cc, rows 4*lb + r.
-//
-// Activation operand.  The 64 x 128-byte group of quantised activations is the same
-// for every column, so each workgroup covers CQ slabs (a 64*CQ-column tile) and
-// stages the group once in LDS with whole-row reads; every wave then reads its A
-// fragments (row l % 16, bytes 16*(l / 16) .. of the K step) from LDS.  Reading it
-// straight from L2 for every 64 columns doubled the L1 traffic and halved the rate.
+// Streaming.  Every workgroup (4 waves, one per CU: the LDS ring below takes most of
+// the CU's 160 KiB) pulls its share of the weights through a D-stage ring in LDS with
+// buffer_load ... lds: a stage is one 128-wide K group of a TN-column tile -- its
+// 32 packed weight rows (TN*128 bytes), the group's 16*MT activation rows (128 bytes
+// each) and its TN column scales.  The copies go straight from memory into LDS, so
+// D-1 stages stay in flight without holding registers; each wave waits for its own
+// copies of the current stage (vmcnt), a barrier makes all of them visible, and the
+// stage's slot is refilled only after every wave is done with it.
 //
 // Work split (stream-K).  Work units are (tile, group) pairs in tile-major order and
 // the P workgroups take equal contiguous ranges, so every CU streams the same number
-// of weight bytes whatever the layer shape.  Inside a workgroup the W = CQ*KS waves
-// are CQ column slabs x KS K-parts: the KS parts of a tile segment run side by side
-// (all waves take the same number of steps; a part that is one group shorter takes
-// a step with zero scales), then reduce through LDS in K order.  A tile that lies in
-// one workgroup's range is written directly; a tile split over several workgroups is
-// summed by the last of them to arrive (a per-tile counter), in workgroup order, so
-// the result does not depend on timing.
+// of weight bytes whatever the layer shape.  A tile that lies inside one workgroup's
+// range is finished there; the pieces of a tile split between workgroups are written
+// as fp32 partial tiles and summed in workgroup order by a small reduction kernel
+// launched right after, so the result does not depend on timing.  Summing them in
+// the same kernel (the last workgroup of a tile to finish reads the others' pieces)
+// measured slower: all of that work falls on a few workgroups at the very end.
+//
+// Operand reads from LDS.  Wave w covers the 64-column slab w % CQ of the tile and the
+// m tiles of part w / CQ of the rows.  Weights: lane (li, lb) = (lane % 16, lane / 16)
+// reads the 16-byte row pieces of rows 16s + 4*lb + i (i = 0..3), columns
+// slab*64 + 4*li .. +3; for column c + cc the four words are 16 consecutive K bytes,
+// i.e. the B operand of an MFMA whose 16 columns are slab*64 + 4*j + cc.  Activations
+// are stored with the 16-byte pieces of row r permuted by XOR with (r / 2) % 8, so the
+// 16 rows of an A fragment fall in 16 different bank groups.
 
-constexpr int kAPitch = 144;           // LDS row pitch of a staged activation group (128 + 16)
+#define I8GS_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9-family format word
 constexpr int kCpolNT = 2;             // non-temporal: streamed weights are not reused
 
-struct DecodePlan {
-    int cq;      // 64-column slabs per tile
-    int tiles;   // column tiles
-    int blocks;  // workgroups sharing the (tile, group) work items
+template <int MT, int TN>
+struct DecodeShape {
+    static constexpr int CQ = TN / 64;              // 64-column slabs per tile
+    static constexpr int MS = 4 / CQ;               // row parts (4 waves = CQ x MS)
+    static constexpr int MTW = MT / MS;             // 16-row m tiles per wave
+    static constexpr int WB = TN * 128;             // weight bytes of a stage
+    static constexpr int AB = MT * 16 * 128;        // activation bytes of a stage
+    static constexpr int SB = 1024;                 // scale slot (TN floats + copies)
+    static constexpr int STAGE = WB + AB + SB;
+    static constexpr int WI = WB / 4096;            // 1 KiB copies per wave: weights
+    static constexpr int AI = AB / 4096;            //   activations
+    static constexpr int LPS = WI + AI + 1;         // memory instructions per wave per stage
+    static constexpr int LPR = TN / 4;              // lanes per packed weight row
+    static constexpr int RPI = 256 / TN;            // packed rows per 1 KiB copy
+    static_assert(CQ * MS == 4 && MT % MS == 0 && AB % 4096 == 0, "unsupported decode shape");
 };
 
-struct DecodeRegs {
-    v4i b[2][4];  // [k step][row i]: 4 columns each (offset-binary codes)
-    v4f sc;       // scales of the 4 columns
-    bool live;    // false on a padding step: its scales are taken as zero when used
-};
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-// Loads of one step: the activation pieces this thread stages, then the weight rows
-// and scales of this wave's slab (activations first, so the wait before staging them
-// leaves the weight loads in flight).
-template <int APT>
-__device__ __forceinline__ void decode_load(DecodeRegs &d, v4i (&areg)[APT], __amdgpu_buffer_rsrc_t wr,
-                                            __amdgpu_buffer_rsrc_t ar, __amdgpu_buffer_rsrc_t sr,
-                                            const int (&a_src)[APT], int g, bool pad, uint32_t row_bytes, int w_lane,
-                                            int s_lane) {
+// Copies of one stage by this wave: its WI pieces of the weight rows, AI pieces of the
+// activation rows and one dword per lane of the scales.
+template <int MT, int TN>
+__device__ __forceinline__ void decode_issue(char *st, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t ar,
+                                             __amdgpu_buffer_rsrc_t sr, int wave, int w_voff,
+                                             const int (&a_voff)[DecodeShape<MT, TN>::AI], int s_voff, int t, int g,
+                                             int N) {
+    using S = DecodeShape<MT, TN>;
 #pragma unroll
-    for (int j = 0; j < APT; ++j) areg[j] = __builtin_amdgcn_raw_buffer_load_b128(ar, a_src[j], g * 128, 0);
-    // Same issue order everywhere (also in the prologue), so the compiler's wait
-    // counts at the loop head stay exact.
-    __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < S::WI; ++j) {
+        const int ins = wave * S::WI + j;
+        const uint32_t so = ((uint32_t)(g * 32 + ins * S::RPI) * (uint32_t)N + (uint32_t)(t * TN)) * 4u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + ins * 1024), 16, w_voff, (int)so, 0, kCpolNT);
+    }
+#pragma unroll
+    for (int j = 0; j < S::AI; ++j) {
+        const int ins = wave * S::AI + j;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, I8GS_LDS(st + S::WB + ins * 1024), 16, a_voff[j], g * 128, 0, 0);
+    }
+    const uint32_t so = ((uint32_t)g * (uint32_t)N + (uint32_t)(t * TN)) * 4u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, I8GS_LDS(st + S::WB + S::AB + wave * 256), 4, s_voff, (int)so, 0, 0);
+}
+
+// One stage on the MFMA units: per column quad cc both K steps for every m tile of
+// this wave (int32, exact), then the fold acc += scale * float(group sum).
+template <int MT, int TN>
+__device__ __forceinline__ void decode_compute(const char *st, int slab, int mpart, int li, int lb,
+                                               float (&acc)[4][DecodeShape<MT, TN>::MTW][4]) {
+    using S = DecodeShape<MT, TN>;
+    v4i b[2][4];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            d.b[s][i] = __builtin_amdgcn_raw_buffer_load_b128(wr, w_lane, (int)((uint32_t)(g * 32 + s * 16 + i) * row_bytes),
-                                                              kCpolNT);
-    __builtin_amdgcn_sched_barrier(0);
-    d.sc = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(sr, s_lane, (int)((uint32_t)g * row_bytes), 0));
-    // Not applied to the loaded scales here: a select on them right after the load
-    // would make the compiler wait for every load in flight.
-    d.live = !pad;
-}
-
-template <int APT, int STRIDE>
-__device__ __forceinline__ void decode_stage(char *lds_buf, const v4i (&areg)[APT], const int (&a_dst)[APT], int tks,
-                                             int pieces) {
-#pragma unroll
-    for (int j = 0; j < APT; ++j)
-        if (tks + j * STRIDE < pieces) *reinterpret_cast<v4i *>(lds_buf + a_dst[j]) = areg[j];
-}
-
-// One step on the MFMA units: the activation fragments of both K steps are read
-// from LDS once, then per column quad cc both K steps for every m tile (int32,
-// exact), then the fold acc += scale * float(group sum).
-template <int MT>
-__device__ __forceinline__ void decode_compute(const DecodeRegs &d, const char *abase, float (&acc)[4][MT][4]) {
-    v4i af[2][MT];
+            b[s][i] = *reinterpret_cast<const v4i *>(st + (16 * s + 4 * lb + i) * (TN * 4) + (slab * 64 + 4 * li) * 4);
+    v4i af[2][S::MTW];
+    const int swz = (li >> 1) & 7;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) af[s][mt] = *reinterpret_cast<const v4i *>(abase + mt * 16 * kAPitch + s * 64);
+        for (int m = 0; m < S::MTW; ++m) {
+            const int row = (mpart * S::MTW + m) * 16 + li;
+            af[s][m] = *reinterpret_cast<const v4i *>(st + S::WB + row * 128 + (((s * 4 + lb) ^ swz) * 16));
+        }
+    const v4f sc = *reinterpret_cast<const v4f *>(st + S::WB + S::AB + (slab * 64 + 4 * li) * 4);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-        v4i p[MT];
+        v4i p[S::MTW];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const v4i bf = v4i{d.b[s][0][cc], d.b[s][1][cc], d.b[s][2][cc], d.b[s][3][cc]} ^ (int)0x80808080;
+            const v4i bf = v4i{b[s][0][cc], b[s][1][cc], b[s][2][cc], b[s][3][cc]} ^ (int)0x80808080;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) p[mt] = mfma_i8(af[s][mt], bf, s == 0 ? v4i{0, 0, 0, 0} : p[mt]);
+            for (int m = 0; m < S::MTW; ++m) p[m] = mfma_i8(af[s][m], bf, s == 0 ? v4i{0, 0, 0, 0} : p[m]);
         }
-        const float sc = d.live ? d.sc[cc] : 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int m = 0; m < S::MTW; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[cc][mt][r] += sc * (float)p[mt][r];
+            for (int r = 0; r < 4; ++r) acc[cc][m][r] += sc[cc] * (float)p[m][r];
     }
 }
 
-// Device-coherent stores and loads (scope "agent": the sc1 cache-policy bit) for the
-// partial tiles exchanged between workgroups.  They are coherent across the XCDs'
-// separate L2 caches, so no cache-wide writeback or invalidate is needed; the writer
-// waits for its stores to complete before it bumps the tile's counter.
-__device__ __forceinline__ void store_coherent(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Units of workgroup b when U units are split evenly over P workgroups:
+// [floor(b*U/P), floor((b+1)*U/P)).  The launch keeps P*U below 2^32.
+__device__ __forceinline__ int range_begin(int b, int U, int P) { return (int)((uint32_t)b * (uint32_t)U / (uint32_t)P); }
+__device__ __forceinline__ int owner_of(int u, int U, int P) {
+    return (int)((((uint32_t)u + 1u) * (uint32_t)P - 1u) / (uint32_t)U);
 }
 
-// Workgroup that owns unit u when U units are split evenly over P workgroups
-// (workgroup b owns [floor(b*U/P), floor((b+1)*U/P))).
-__device__ __forceinline__ int owner_of(int64_t u, int64_t U, int P) { return (int)(((u + 1) * P - 1) / U); }
+// bf16(a_scale[row] * acc) of this lane's 4 adjacent columns, packed for one 8-byte store.
+__device__ __forceinline__ v2i pack_y(float a, float c0, float c1, float c2, float c3) {
+    return v2i{(int)(f32_to_bf16_bits(a * c0) | ((uint32_t)f32_to_bf16_bits(a * c1) << 16)),
+               (int)(f32_to_bf16_bits(a * c2) | ((uint32_t)f32_to_bf16_bits(a * c3) << 16))};
+}
 
-template <int MT, int CQ, int KS>
-__global__ __launch_bounds__(CQ * KS * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void w8a8_decode_kernel(
-    const int8_t *__restrict__ qa, const float *__restrict__ a_scale, const int32_t *__restrict__ qweight,
-    const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ldy, int M, int N, int K, int tiles,
-    int P, float *__restrict__ part, int *__restrict__ cnt) {
-    constexpr int TN = 64 * CQ;
-    constexpr int NACC = 16 * MT;                                 // fp32 accumulators per lane
-    constexpr int ROWS = 16 * MT;
-    constexpr int APIECES = ROWS * 8;                             // 16-byte pieces of one staged group
-    constexpr int APT = (APIECES + CQ * 64 - 1) / (CQ * 64);      // pieces per thread of a K part
-    constexpr int ABUF = ROWS * kAPitch;                          // bytes of one staged group
-    constexpr int A_LDS = 2 * KS * ABUF;
-    constexpr int R_LDS = (KS - 1) * CQ * NACC * 64 * 4;
-    constexpr int LDS_BYTES = A_LDS > R_LDS ? A_LDS : R_LDS;
-    static_assert((16 * MT / KS) % 4 == 0, "each wave must finish whole (row, 4-column) pieces");
-    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-    __shared__ int s_flag;
+template <int MT, int TN, int D>
+__global__ __launch_bounds__(256) void w8a8_decode_kernel(const int8_t *__restrict__ qa,
+                                                          const float *__restrict__ a_scale,
+                                                          const int32_t *__restrict__ qweight,
+                                                          const float *__restrict__ w_scale,
+                                                          uint16_t *__restrict__ y, int64_t ldy, int M, int N, int K,
+                                                          int tiles, int P, float *__restrict__ part) {
+    using S = DecodeShape<MT, TN>;
+    constexpr int MTW = S::MTW;
+    static_assert(D >= 2 && D <= 8 && D * S::STAGE <= 160 * 1024, "LDS ring too large");
+    // One LDS object only: with a second one the compiler can no longer tell the
+    // ring's reads from the copies in flight and waits for all of them.
+    __shared__ __attribute__((aligned(1024))) char lds[D * S::STAGE];
 
     const int b = blockIdx.x;
     const int G = K >> 7;
-    const int64_t U = (int64_t)tiles * G;
-    const int64_t u0 = (int64_t)b * U / P, u1 = (int64_t)(b + 1) * U / P;
+    const int U = tiles * G;
+    const int u0 = range_begin(b, U, P), u1 = range_begin(b + 1, U, P);
     if (u0 >= u1) return;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps group offsets in SGPRs
-    const int cq = wave % CQ, ks = wave / CQ;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slab = wave % S::CQ, mpart = wave / S::CQ;
     const int li = lane & 15, lb = lane >> 4;
-    const int tks = cq * 64 + lane;  // thread index among the CQ waves of this K part
-    const int t_first = (int)(u0 / G), t_last = (int)((u1 - 1) / G);
+    const int row0 = mpart * MTW * 16 + 4 * lb;  // this lane's rows: row0 + 16*m + r
+    const int lcol = slab * 64 + 4 * li;         // this lane's 4 columns within a tile
 
+    // byte offsets fit 32 bits: K*N < 2^32, M*K < 2^32 and M*ldy*2 < 2^31 are checked
+    // before launch
     const __amdgpu_buffer_rsrc_t wr =
         __builtin_amdgcn_make_buffer_rsrc((void *)qweight, 0, (int)((uint32_t)K * (uint32_t)N), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t ar =
         __builtin_amdgcn_make_buffer_rsrc((void *)qa, 0, (int)((uint32_t)M * (uint32_t)K), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t sr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)w_scale, 0, (int)((uint32_t)(K >> 7) * (uint32_t)N * 4u), kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void *)w_scale, 0, (int)((uint32_t)G * (uint32_t)N * 4u), kRsrcWord3);
+    // Output stores go through a buffer descriptor whose range check drops those
+    // outside y (rows >= M; columns >= N are sent past the end explicitly).
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)y, 0, (int)(((uint32_t)(M - 1) * (uint32_t)ldy + (uint32_t)N) * 2u), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)part, 0, (int)((uint32_t)P * 2u * (uint32_t)(64 * TN * 4)), kRsrcWord3);
 
-    // Activation staging: piece pc = tks + j*CQ*64 is row pc / 8, bytes (pc % 8) * 16.
-    int a_src[APT], a_dst[APT];
+    // Per-lane parts of the copy addresses.  Weights: packed row lane / LPR of the
+    // copy, columns 4*(lane % LPR) .. +3.  Activations: LDS slot lane % 8 of row
+    // 8*copy + lane / 8 holds piece slot ^ ((row / 2) % 8) of that row (rows past M
+    // repeat row M - 1; their results are never stored).  Scales: column
+    // (64*wave + lane) % TN.
+    const int w_voff = (lane / S::LPR) * N * 4 + (lane % S::LPR) * 16;
+    int a_voff[S::AI];
 #pragma unroll
-    for (int j = 0; j < APT; ++j) {
-        const int pc = min(tks + j * CQ * 64, APIECES - 1);
-        a_src[j] = (int)((uint32_t)min(pc >> 3, M - 1) * (uint32_t)K + (uint32_t)(pc & 7) * 16u);
-        a_dst[j] = ks * ABUF + (pc >> 3) * kAPitch + (pc & 7) * 16;
+    for (int j = 0; j < S::AI; ++j) {
+        const int row = (wave * S::AI + j) * 8 + (lane >> 3);
+        const int piece = (lane & 7) ^ ((row >> 1) & 7);
+        a_voff[j] = (int)((uint32_t)min(row, M - 1) * (uint32_t)K + (uint32_t)piece * 16u);
     }
-    const int a_frag = li * kAPitch + lb * 16;  // + ks*ABUF + mt*16*kAPitch + s*64
+    const int s_voff = ((wave * 64 + lane) % TN) * 4;
 
-    for (int t = t_first; t <= t_last; ++t) {
-        const int64_t tb = (int64_t)t * G;
-        const int ga = (int)(max(u0, tb) - tb), gb = (int)(min(u1, tb + G) - tb);
-        const int ng = gb - ga;
-        const int ka = ga + (ks * ng) / KS, nk = ga + ((ks + 1) * ng) / KS - ka;
-        const int steps = (ng + KS - 1) / KS;  // same for every wave
-        const int n0 = t * TN + cq * 64;
-        const int col0 = min(n0 + 4 * li, N - 4);  // N % 8 == 0, so a clamped quad stays inside the row
-        // byte offsets fit 32 bits: K*N < 2^32 is checked before launch
-        const int w_lane = (int)(((uint32_t)(4 * lb) * (uint32_t)N + (uint32_t)col0) * 4u), s_lane = col0 * 4;
+    // Row scales of this lane's output rows (4 consecutive rows per m tile; rows past
+    // M read as 0), loaded and waited for before the ring starts: memory operations
+    // complete in order, so a wait for a load issued later would drain the ring.
+    const __amdgpu_buffer_rsrc_t asr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)a_scale, 0, (int)((uint32_t)M * 4u), kRsrcWord3);
+    v4f as[MTW];
+#pragma unroll
+    for (int m = 0; m < MTW; ++m)
+        as[m] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(asr, (row0 + 16 * m) * 4, 0, 0));
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) asm volatile("" ::"v"(as[m]));
 
-        float acc[4][MT][4];
+    int ti = u0 / G, gi = u0 - (u0 / G) * G;  // next unit to copy
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[cc][mt][r] = 0.0f;
-
-        // Ping-pong over steps: while step i computes, the loads of step i+1 are in
-        // flight.  The body is straight-line -- a step past this part's end re-reads a
-        // valid group and has zero scales, also for the second half of the last pair
-        // -- so the compiler's wait counts stay exact; sched_barrier keeps each
-        // prefetch from sinking below the current step's waits.
-        {
-            const uint32_t row_bytes = (uint32_t)N * 4u;
-            char *abuf0 = lds + ks * ABUF;
-            char *abuf1 = lds + KS * ABUF + ks * ABUF;
-            DecodeRegs r0, r1;
-            v4i areg[APT];
-            decode_load<APT>(r0, areg, wr, ar, sr, a_src, nk > 0 ? ka : ga, nk <= 0, row_bytes, w_lane, s_lane);
-            for (int i = 0; i < steps; i += 2) {
-                decode_stage<APT, CQ * 64>(lds, areg, a_dst, tks, APIECES);
-                decode_load<APT>(r1, areg, wr, ar, sr, a_src, nk > 0 ? ka + min(i + 1, nk - 1) : ga, i + 1 >= nk,
-                                 row_bytes, w_lane, s_lane);
-                __builtin_amdgcn_sched_barrier(0);
-                lds_barrier();
-                decode_compute<MT>(r0, abuf0 + a_frag, acc);
-                __builtin_amdgcn_sched_barrier(0);
-                decode_stage<APT, CQ * 64>(lds + KS * ABUF, areg, a_dst, tks, APIECES);
-                decode_load<APT>(r0, areg, wr, ar, sr, a_src, nk > 0 ? ka + min(i + 2, nk - 1) : ga, i + 2 >= nk,
-                                 row_bytes, w_lane, s_lane);
-                __builtin_amdgcn_sched_barrier(0);
-                lds_barrier();
-                decode_compute<MT>(r1, abuf1 + a_frag, acc);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+    for (int s = 0; s < D - 1; ++s) {
+        if (u0 + s < u1) {
+            decode_issue<MT, TN>(lds + s * S::STAGE, wr, ar, sr, wave, w_voff, a_voff, s_voff, ti, gi, N);
+            if (++gi == G) { gi = 0; ++ti; }
         }
+    }
 
-        // Reduce the K parts into the ks == 0 waves, in K order.
-        if constexpr (KS > 1) {
-            __syncthreads();  // the LDS staging area is reused below
-            float *red = reinterpret_cast<float *>(lds);
-            if (ks > 0) {
-                float *dst = red + ((ks - 1) * CQ + cq) * NACC * 64;
-                int i = 0;
+    const int t_first = u0 / G;
+    int tc = t_first, gc = u0 - t_first * G;  // unit being computed
+    int seg_g0 = gc;                          // first group of the current tile segment
+    float acc[4][MTW][4];
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc)
+    for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
+        for (int m = 0; m < MTW; ++m)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r, ++i) dst[i * 64 + lane] = acc[cc][mt][r];
-            }
-            __syncthreads();
-            if (ks == 0) {
-#pragma unroll
-                for (int k2 = 1; k2 < KS; ++k2) {
-                    const float *src = red + ((k2 - 1) * CQ + cq) * NACC * 64;
-                    int i = 0;
-#pragma unroll
-                    for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r, ++i) acc[cc][mt][r] += src[i * 64 + lane];
-                }
-            }
-            __syncthreads();  // before the next segment stages activations again
+            for (int r = 0; r < 4; ++r) acc[cc][m][r] = 0.0f;
+
+    int slot = 0;
+    for (int u = u0; u < u1; ++u) {
+        // Memory operations complete in order; the D-2 stages after this one are the
+        // youngest copies, so this count waits for this stage.  Stores issued at the
+        // end of a tile segment are younger still and make this wait longer, not
+        // shorter (counting them exactly, so they stay in flight, measured slower).
+        if (u + D - 2 < u1) wait_vmcnt<(D - 2) * S::LPS>();
+        else wait_vmcnt<0>();
+        barrier_only();
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + D - 1 < u1) {
+            const int ns = slot == 0 ? D - 1 : slot - 1;  // slot of the previous stage, now free
+            decode_issue<MT, TN>(lds + ns * S::STAGE, wr, ar, sr, wave, w_voff, a_voff, s_voff, ti, gi, N);
+            if (++gi == G) { gi = 0; ++ti; }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        decode_compute<MT, TN>(lds + slot * S::STAGE, slab, mpart, li, lb, acc);
+        slot = slot == D - 1 ? 0 : slot + 1;
 
-        if (ng < G) {
-            // Split tile: publish this workgroup's partial (layout [cq][m tile][row][quad]),
-            // count arrivals, and let the last arrival sum the partials in workgroup order.
-            // The sum is spread over all W waves, each re-reading its share of every
-            // partial (its own included) with the loads of up to four workgroups in flight.
-            const int slot = (t == t_first) ? 0 : 1;
-            if (ks == 0) {
-                float *mine = part + (((int64_t)b * 2 + slot) * CQ + cq) * NACC * 64;
+        if (gc == G - 1 || u == u1 - 1) {
+            const int col = tc * TN + lcol;
+            if (seg_g0 == 0 && gc == G - 1) {
+                // whole tile: y = bf16(a_scale[row] * sum), 4 columns per store
+                const uint32_t cbase = col < N ? (uint32_t)col * 2u : 0x80000000u;
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+                for (int m = 0; m < MTW; ++m)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t off = cbase + (uint32_t)(row0 + 16 * m + r) * (uint32_t)ldy * 2u;
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            pack_y(as[m][r], acc[0][m][r], acc[1][m][r], acc[2][m][r], acc[3][m][r]), yr,
+                            (int)(col < N ? off : 0x80000000u), 0, 0);
+                    }
+            } else {
+                // piece of a split tile: fp32 [row][TN] in slot 0 (first tile of this
+                // range) or 1 (last tile)
+                const int soff = (b * 2 + (tc == t_first ? 0 : 1)) * (64 * TN * 4);
+#pragma unroll
+                for (int m = 0; m < MTW; ++m)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-#pragma unroll
-                        for (int cc = 0; cc < 4; ++cc)
-                            store_coherent(mine + ((mt * 4 + r) * 4 + cc) * 64 + lane, acc[cc][mt][r]);
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(v4i, v4f{acc[0][m][r], acc[1][m][r], acc[2][m][r], acc[3][m][r]}),
+                            pr, ((row0 + 16 * m + r) * TN + lcol) * 4, soff, 0);
             }
-            __syncthreads();
-            const int bf = owner_of(tb, U, P), bl = owner_of(tb + G - 1, U, P);
-            if (threadIdx.x == 0) s_flag = atomicAdd(cnt + t, 1);
-            __syncthreads();
-            if (s_flag != bl - bf) continue;
-            asm volatile("" ::: "memory");
-            constexpr int VPW = CQ * NACC / (CQ * KS);  // values per lane per wave (a multiple of 4)
-            constexpr int QB = VPW >= 64 ? 1 : (VPW >= 32 ? 2 : 4);  // partials loaded at once (register budget)
-            const int v0 = wave * VPW;                  // first value of this wave in [cq][m tile][row][quad] order
-            float sum[VPW];
-            for (int q0 = bf; q0 <= bl; q0 += QB) {
-                float v[QB][VPW];
 #pragma unroll
-                for (int j = 0; j < QB; ++j) {
-                    const int q = min(q0 + j, bl);
-                    const int64_t qb = (int64_t)q * U / P;
-                    const int qslot = (t == (int)(qb / G)) ? 0 : 1;
-                    const float *src = part + ((int64_t)q * 2 + qslot) * CQ * NACC * 64 + (int64_t)v0 * 64;
+            for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-                    for (int k = 0; k < VPW; ++k) v[j][k] = load_coherent(src + k * 64 + lane);
-                }
+                for (int m = 0; m < MTW; ++m)
 #pragma unroll
-                for (int j = 0; j < QB; ++j)
-                    if (q0 + j <= bl) {
-#pragma unroll
-                        for (int k = 0; k < VPW; ++k) sum[k] = (q0 + j == bf) ? v[j][k] : sum[k] + v[j][k];
-                    }
-            }
-            // Write this wave's share: VPW/4 (m tile, row) pairs x 4 adjacent columns.
-            const int wcq = v0 / NACC;
-            const int colw = t * TN + wcq * 64 + 4 * li;
-            if (colw < N) {
-#pragma unroll
-                for (int k = 0; k < VPW; k += 4) {
-                    const int pr = ((v0 % NACC) + k) >> 2;  // m tile * 4 + row index r
-                    const int row = (pr >> 2) * 16 + lb * 4 + (pr & 3);
-                    if (row < M) {
-                        const float as = a_scale[row];
-                        const uint32_t lo = f32_to_bf16_bits(as * sum[k]) | ((uint32_t)f32_to_bf16_bits(as * sum[k + 1]) << 16);
-                        const uint32_t hi =
-                            f32_to_bf16_bits(as * sum[k + 2]) | ((uint32_t)f32_to_bf16_bits(as * sum[k + 3]) << 16);
-                        *reinterpret_cast<v2i *>(y + (int64_t)row * ldy + colw) = v2i{(int)lo, (int)hi};
-                    }
-                }
-            }
-            if (threadIdx.x == 0) cnt[t] = 0;  // leave the counter at zero for the next call
-            continue;
+                    for (int r = 0; r < 4; ++r) acc[cc][m][r] = 0.0f;
+            seg_g0 = 0;
         }
-
-        // Epilogue (ks == 0 waves): y = bf16(a_scale[row] * sum), 4 adjacent columns per 8-byte store.
-        const int col = n0 + 4 * li;
-        if (ks == 0 && col < N) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = mt * 16 + lb * 4 + r;
-                    if (row < M) {
-                        const float as = a_scale[row];
-                        const uint32_t lo = f32_to_bf16_bits(as * acc[0][mt][r]) |
-                                            ((uint32_t)f32_to_bf16_bits(as * acc[1][mt][r]) << 16);
-                        const uint32_t hi = f32_to_bf16_bits(as * acc[2][mt][r]) |
-                                            ((uint32_t)f32_to_bf16_bits(as * acc[3][mt][r]) << 16);
-                        *reinterpret_cast<v2i *>(y + (int64_t)row * ldy + col) = v2i{(int)lo, (int)hi};
-                    }
-                }
-        }
+        if (++gc == G) { gc = 0; ++tc; }
     }
+}
+
+// Sums the pieces of every split tile in workgroup order and writes y.  Block x takes
+// the tile holding the boundary between workgroups x and x + 1 when that boundary lies
+// strictly inside a tile and is the first such boundary of the tile; block y covers
+// 256 (row, 4-column) pieces of it.
+template <int TN>
+__global__ __launch_bounds__(256) void w8a8_splitk_reduce(const float *__restrict__ part,
+                                                          const float *__restrict__ a_scale,
+                                                          uint16_t *__restrict__ y, int64_t ldy, int M, int N,
+                                                          int tiles, int G, int P) {
+    const int U = tiles * G;
+    const int bi = blockIdx.x + 1;
+    const int ub = range_begin(bi, U, P);
+    const int t = ub / G;
+    if (ub == t * G) return;
+    if (bi > 1 && range_begin(bi - 1, U, P) > t * G) return;
+    constexpr int QPR = TN / 4;
+    const int idx = blockIdx.y * 256 + threadIdx.x;
+    const int row = idx / QPR, q = idx % QPR;
+    const int col = t * TN + 4 * q;
+    if (row >= M || col >= N) return;
+    const int bf = owner_of(t * G, U, P), bl = owner_of(t * G + G - 1, U, P);
+    const float *src = part + row * TN + 4 * q;
+    v4f sum;
+    for (int w0 = bf; w0 <= bl; w0 += 8) {
+        // up to 8 pieces in flight at once, summed in workgroup order
+        v4f v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int w = w0 + j;
+            if (w > bl) break;
+            const int sl = range_begin(w, U, P) / G == t ? 0 : 1;
+            v[j] = *reinterpret_cast<const v4f *>(src + (int64_t)(w * 2 + sl) * (64 * TN));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (w0 + j <= bl) sum = (w0 + j == bf) ? v[j] : sum + v[j];
+    }
+    *reinterpret_cast<v2i *>(y + (int64_t)row * ldy + col) = pack_y(a_scale[row], sum[0], sum[1], sum[2], sum[3]);
 }
 
 int device_cu_count() {
@@ -392,56 +366,48 @@ int device_cu_count() {
     return cached[dev];
 }
 
-#ifndef I8GS_DECODE_CQ
-#define I8GS_DECODE_CQ 0  // 0 = choose per shape
+#ifndef I8GS_DECODE_TN
+#define I8GS_DECODE_TN 128
 #endif
-#ifndef I8GS_DECODE_KS
-#define I8GS_DECODE_KS 1
+#ifndef I8GS_DECODE_STAGES
+#define I8GS_DECODE_STAGES 3
 #endif
-#ifndef I8GS_DECODE_WG_PER_CU
-#define I8GS_DECODE_WG_PER_CU 2
-#endif
+
+struct DecodePlan {
+    int tn;      // tile columns
+    int tiles;   // column tiles
+    int blocks;  // workgroups sharing the (tile, group) units
+};
 
 DecodePlan decode_plan(int M, int N, int K, int workgroups) {
     (void)M;
     DecodePlan p;
-    // Wider tiles share each staged activation group across more columns (less L2
-    // traffic); narrower tiles make smaller partial tiles where tiles are split.
-    int cq = I8GS_DECODE_CQ;
-    if (cq == 0) cq = 4;
-    if (cq != 2) cq = 4;
-    p.cq = cq;
-    p.tiles = (N + 64 * cq - 1) / (64 * cq);
+    p.tn = I8GS_DECODE_TN;
+    p.tiles = (N + p.tn - 1) / p.tn;
     const int64_t U = (int64_t)p.tiles * (K / kGroup);
-    int64_t P = workgroups > 0 ? workgroups : (int64_t)device_cu_count() * I8GS_DECODE_WG_PER_CU;
+    int64_t P = workgroups > 0 ? workgroups : (int64_t)device_cu_count();
     if (P > U) P = U;
+    if (P * U >= (int64_t(1) << 32)) P = ((int64_t(1) << 32) - 1) / U;  // 32-bit range arithmetic
     if (P < 1) P = 1;
-    // Split tiles need a counter each; with one workgroup per tile no tile is split.
-    if (p.tiles > kMaxCounters) P = p.tiles;
     p.blocks = (int)P;
     return p;
 }
 
-// Partial-sum bytes after the counter region: two partial tiles per workgroup.
-size_t decode_workspace(const DecodePlan &p, int M) {
-    const int MT = (M + 15) / 16;
-    return align256(size_t(p.blocks) * 2 * p.cq * 16 * MT * 64 * sizeof(float));
-}
+// Two fp32 partial tiles (64 rows) per workgroup.
+size_t decode_workspace(const DecodePlan &p) { return align256(size_t(p.blocks) * 2 * 64 * p.tn * sizeof(float)); }
 
-template <int MT, int CQ>
-hipError_t launch_decode_cq(const W8A8Args &a, const DecodePlan &p, hipStream_t st) {
-    constexpr int KS = I8GS_DECODE_KS;
-    w8a8_decode_kernel<MT, CQ, KS><<<p.blocks, CQ * KS * 64, 0, st>>>(a.qa, a.a_scale, a.qweight, a.w_scale, a.y, a.ldy, a.M,
-                                                            a.N, a.K, p.tiles, p.blocks, (float *)a.ws, a.counters);
+template <int MT, int TN>
+hipError_t launch_decode(const W8A8Args &a, const DecodePlan &p, hipStream_t st) {
+    constexpr int D = I8GS_DECODE_STAGES;
+    float *part = (float *)a.ws;
+    w8a8_decode_kernel<MT, TN, D><<<p.blocks, 256, 0, st>>>(a.qa, a.a_scale, a.qweight, a.w_scale, a.y, a.ldy, a.M,
+                                                             a.N, a.K, p.tiles, p.blocks, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.blocks < 2) return e;
+    const dim3 grid(p.blocks - 1, (a.M * (TN / 4) + 255) / 256);
+    w8a8_splitk_reduce<TN><<<grid, 256, 0, st>>>(part, a.a_scale, a.y, a.ldy, a.M, a.N, p.tiles, a.K / kGroup,
+                                                 p.blocks);
     return hipGetLastError();
-}
-
-template <int MT>
-hipError_t launch_decode_mt(const W8A8Args &a, const DecodePlan &p, hipStream_t st) {
-    switch (p.cq) {
-        case 2: return launch_decode_cq<MT, 2>(a, p, st);
-        default: return launch_decode_cq<MT, 4>(a, p, st);
-    }
 }
 
 // ------------------------------------------------------------------ tiled kernel (M > 64)
@@ -561,20 +527,19 @@ static bool use_decode(int M, int kernel) {
     return M <= 64;
 }
 
+// The decode kernel addresses y with 32-bit offsets.
+bool decode_y_fits(int64_t M, int64_t ldy) { return M * ldy * 2 < (int64_t(1) << 31); }
+
 size_t w8a8_gemm_workspace(int M, int N, int K, int kernel, int workgroups) {
-    if (use_decode(M, kernel)) return decode_workspace(decode_plan(M, N, K, workgroups), M);
+    if (use_decode(M, kernel)) return decode_workspace(decode_plan(M, N, K, workgroups));
     return 0;
 }
 
 hipError_t launch_w8a8_gemm(const W8A8Args &a, hipStream_t s) {
-    if (a.P == nullptr && use_decode(a.M, a.kernel)) {
+    if (a.P == nullptr && use_decode(a.M, a.kernel) && decode_y_fits(a.M, a.ldy)) {
         const DecodePlan p = decode_plan(a.M, a.N, a.K, a.workgroups);
-        switch ((a.M + 15) / 16) {
-            case 1: return launch_decode_mt<1>(a, p, s);
-            case 2: return launch_decode_mt<2>(a, p, s);
-            case 3: return launch_decode_mt<3>(a, p, s);
-            default: return launch_decode_mt<4>(a, p, s);
-        }
+        if (a.M <= 32) return launch_decode<2, I8GS_DECODE_TN>(a, p, s);
+        return launch_decode<4, I8GS_DECODE_TN>(a, p, s);
     }
     dim3 grid((a.N + kTB - 1) / kTB, (a.M + kTB - 1) / kTB);
     if (a.P)

@@ -81,6 +81,7 @@ def _w8a8(lib, x=A, ldx=512, qa=NUL, a_s=NUL, qw=A, ws=A, y=A, ldy=256, M=8, N=2
     (dict(kernel=7), 1, "I8GS_KERNEL"),
     (dict(split=-2), 1, "decode_workgroups"),
     (dict(kernel=1, M=65), 2, "decode kernel"),
+    (dict(kernel=1, ldy=1 << 28), 2, "M*ldy*2"),
 ])
 def test_w8a8_validation(lib, kwargs, status, needle):
     rc = _w8a8(lib, **kwargs)
@@ -125,5 +126,6 @@ def test_workspace_sizes(lib):
         i8.workspace_bytes(i8.OP_W8A8, 8, 256, 500)
     with pytest.raises(ValueError):
         i8.workspace_bytes(7, 8, 256, 512)
-    # the decode kernel adds two partial tiles per workgroup
-    assert i8.workspace_bytes(i8.OP_W8A8, 64, 6144, 5120, i8.KERNEL_DECODE, 3) > 65536 + 64 * 5120 + 3 * 2 * 16384
+    # the decode kernel adds two fp32 partial tiles (64 rows x 128 columns) per workgroup
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 6144, 5120, i8.KERNEL_DECODE, 3) == (
+        65536 + 64 * 5120 + 256 + 3 * 2 * 64 * 128 * 4)
