@@ -110,7 +110,8 @@ int quant_act_per_token(const void *x, int64_t ldx, int64_t M, int64_t K, int8_t
  * (I8GS_OP_W4A16) needs for these sizes.  Layout: a fixed 64 KiB region of
  * split-K arrival counters at offset 0, then (W8A8) the quantised activations used
  * when x is passed (M*K bytes + 4*M, each piece rounded up to 256 bytes; always
- * counted), then the split-K partial sums.  Returns 0 when no workspace is needed
+ * counted), then the split-K partial sums (decode kernel with K split: T*S fp32
+ * pieces of 64 rows by the kernel's chunk width rounded up to 32 columns).  Returns 0 when no workspace is needed
  * (W4A16 without a K split) and (size_t)-1 for invalid arguments.
  *
  * Workspace contract: the counter region must be zero when a call starts, and
@@ -140,11 +141,12 @@ int gemm_w8a8_g128(const void *x, int64_t ldx, const int8_t *qa, const float *a_
 
 /*
  * gemm_w8a8_g128 with the kernel chosen by the caller: kernel is one of
- * I8GS_KERNEL_*; decode_workgroups (decode kernel only) is the number of
- * workgroups that share the (128-column tile x 128-wide K group) work items
- * evenly, 0 for the automatic choice (one per compute unit); it is clamped to the
- * number of work items.  Every choice computes the same exact group sums; only
- * the fp32 fold order differs.  I8GS_KERNEL_DECODE is rejected when M > 64 or
+ * I8GS_KERNEL_*; decode_workgroups (decode kernel only) is the target number of
+ * workgroups, 0 for the automatic choice (one per compute unit).  The decode
+ * kernel splits the columns into T tiles of multiples of 8 columns and, for narrow
+ * layers, K into S <= 8 parts of whole 128-wide groups (S = ceil(64 * target / N),
+ * T = target / S, both clamped to the layer), so it runs T*S workgroups.  Every
+ * choice computes the same exact group sums; only the fp32 fold order differs.  I8GS_KERNEL_DECODE is rejected when M > 64 or
  * when M*ldy*2 >= 2^31 (32-bit output offsets); I8GS_KERNEL_AUTO takes the tiled
  * kernel in that case.
  */

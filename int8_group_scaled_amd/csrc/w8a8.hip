@@ -18,11 +18,12 @@
 // two's-complement int8 value of q.
 //
 // Two kernels:
-//  * decode (M <= 64): bound by streaming the weights from HBM.  One workgroup per
-//    CU streams an equal share of (tile, group) units through an LDS ring filled by
-//    direct buffer-to-LDS copies; tiles split between workgroups are summed in a
-//    fixed order by a small reduction kernel.
+//  * decode (M <= 64): bound by streaming the weights from HBM.  About one
+//    workgroup per CU streams its columns (and, for narrow layers, a part of K)
+//    through an LDS ring filled by direct buffer-to-LDS copies.
 //  * tiled (M > 64): LDS-staged 128x128 tiles, four waves of 64x64.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace i8gs {
@@ -42,52 +43,76 @@ __device__ __forceinline__ v4i flip(v4i v) {
 
 // ------------------------------------------------------------------ decode kernel
 //
-// Streaming.  Every workgroup (4 waves, one per CU: the LDS ring below takes most of
-// the CU's 160 KiB) pulls its share of the weights through a D-stage ring in LDS with
-// buffer_load ... lds: a stage is one 128-wide K group of a TN-column tile -- its
-// 32 packed weight rows (TN*128 bytes), the group's 16*MT activation rows (128 bytes
-// each) and its TN column scales.  The copies go straight from memory into LDS, so
-// D-1 stages stay in flight without holding registers; each wave waits for its own
-// copies of the current stage (vmcnt), a barrier makes all of them visible, and the
-// stage's slot is refilled only after every wave is done with it.
+// Work split.  The launch is a grid of T column tiles x S K-splits, about one
+// workgroup per CU.  Tile t covers columns [8*floor(t*N/8/T), 8*floor((t+1)*N/8/T));
+// split s covers groups [floor(s*G/S), floor((s+1)*G/S)) of the G = K/128 groups.
+// Wide layers take S = 1: every workgroup owns whole columns, streams all of K for
+// them and writes y itself; its columns are walked in chunks of at most TN.  Narrow
+// layers take S > 1 so that a tile stays about 64 columns wide or more (each streamed
+// weight byte then costs at most one activation byte); the S workgroups of a tile
+// each write an fp32 piece and the last of them to finish sums the pieces in split
+// order, so the result does not depend on timing.  The S workgroups of a tile are T
+// apart in launch order.
 //
-// Work split (stream-K).  Work units are (tile, group) pairs in tile-major order and
-// the P workgroups take equal contiguous ranges, so every CU streams the same number
-// of weight bytes whatever the layer shape.  A tile that lies inside one workgroup's
-// range is finished there; the pieces of a tile split between workgroups are written
-// as fp32 partial tiles and summed in workgroup order by a small reduction kernel
-// launched right after, so the result does not depend on timing.  Summing them in
-// the same kernel (the last workgroup of a tile to finish reads the others' pieces)
-// measured slower: all of that work falls on a few workgroups at the very end.
+// Streaming.  Each workgroup (4 waves; one per CU, the LDS ring takes most of the
+// CU's 160 KiB) pulls its units -- (chunk, group) pairs, chunk-major -- through a
+// D-stage ring in LDS filled by buffer_load ... lds: a stage holds the chunk's 32
+// packed weight rows of the group (row-major, TN*4 bytes per row), the group's
+// 32*M2 activation rows (128 bytes each) and the chunk's column scales.  The copies
+// go straight from memory to LDS, so D-1 stages stay in flight without holding
+// registers; each wave waits for its own copies of the current stage (vmcnt), a
+// barrier makes all of them visible, and the slot is refilled only after every wave
+// is done with it.  Copies beyond the chunk's columns repeat its last piece (a cache
+// hit), so every wave issues the same number of copies per stage.
 //
-// Operand reads from LDS.  Wave w covers the 64-column slab w % CQ of the tile and the
-// m tiles of part w / CQ of the rows.  Weights: lane (li, lb) = (lane % 16, lane / 16)
-// reads the 16-byte row pieces of rows 16s + 4*lb + i (i = 0..3), columns
-// slab*64 + 4*li .. +3; for column c + cc the four words are 16 consecutive K bytes,
-// i.e. the B operand of an MFMA whose 16 columns are slab*64 + 4*j + cc.  Activations
-// are stored with the 16-byte pieces of row r permuted by XOR with (r / 2) % 8, so the
-// 16 rows of an A fragment fall in 16 different bank groups.
+// MFMA.  v_mfma_i32_32x32x32_i8: lane l holds row (l % 32) of A and column (l % 32)
+// of B, 16 consecutive K bytes at 16*(l / 32) of a 32-wide K step (A and B use the
+// same placement, so the product is the plain dot product); the 32x32 int32 result
+// puts column l % 32, rows 8*(i / 4) + 4*(l / 32) + i % 4 in register i of lane l.
+// On gfx950 this shape runs at about 2.6x the rate of the 16x16x64 one (measured).
+// A is the activation rows (m tile of 32 tokens); B is a 32-column fragment of the
+// chunk: lane (col, h) = (l % 32, l / 32) reads, for K step ks, the words of packed
+// rows 8*ks + 4*h + i (i = 0..3) of its column -- 16 consecutive K bytes.  Wave w
+// takes m tile w % 2 and fragments w / 2 + 2j (M > 32), or fragments w + 4j (M <= 32).
+// Activations are stored with the 16-byte pieces of row r permuted by XOR with r % 8,
+// so the rows read together fall in different bank groups.
 
 #define I8GS_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9-family format word
 constexpr int kCpolNT = 2;             // non-temporal: streamed weights are not reused
+constexpr int kCpolSC1 = 16;           // device-coherent (across the XCDs' L2 caches)
+constexpr int kMaxSplits = 8;
 
-template <int MT, int TN>
+#ifndef I8GS_DECODE_SPLIT_CHAIN
+#define I8GS_DECODE_SPLIT_CHAIN 0  // 1: each fragment's group sum as two MFMA chains of two K steps
+#endif
+
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ v16i mfma32_i8(v4i a, v4i b, v16i c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+template <int M2, int TN, int W>
 struct DecodeShape {
-    static constexpr int CQ = TN / 64;              // 64-column slabs per tile
-    static constexpr int MS = 4 / CQ;               // row parts (4 waves = CQ x MS)
-    static constexpr int MTW = MT / MS;             // 16-row m tiles per wave
-    static constexpr int WB = TN * 128;             // weight bytes of a stage
-    static constexpr int AB = MT * 16 * 128;        // activation bytes of a stage
-    static constexpr int SB = 1024;                 // scale slot (TN floats + copies)
+    static_assert((M2 == 1 || M2 == 2) && (W == 4 || W == 8) && TN % 8 == 0 && TN >= 8 && TN <= 256,
+                  "unsupported decode shape");
+    static constexpr int NF = (TN + 31) / 32;          // 32-column fragments of a chunk
+    static constexpr int WPM = W / M2;                 // waves per m tile
+    static constexpr int NFW = (NF + WPM - 1) / WPM;   // fragments per wave
+    static constexpr int PPR = TN / 4;                 // 16-byte pieces per weight row
+    // Copies are issued by waves 0..3 (the others only compute).
+    static constexpr int WI = (TN + 31) / 32;          // 1 KiB weight copies per copying wave per stage
+    static constexpr int WB = WI * 4096;               // weight bytes of a stage (TN*128 used)
+    static constexpr int AI = M2;                      // 1 KiB activation copies per copying wave
+    static constexpr int AB = M2 * 32 * 128;           // activation bytes of a stage
+    static constexpr int SB = 1024;                    // scales (TN floats; copies past TN unused)
     static constexpr int STAGE = WB + AB + SB;
-    static constexpr int WI = WB / 4096;            // 1 KiB copies per wave: weights
-    static constexpr int AI = AB / 4096;            //   activations
-    static constexpr int LPS = WI + AI + 1;         // memory instructions per wave per stage
-    static constexpr int LPR = TN / 4;              // lanes per packed weight row
-    static constexpr int RPI = 256 / TN;            // packed rows per 1 KiB copy
-    static_assert(CQ * MS == 4 && MT % MS == 0 && AB % 4096 == 0, "unsupported decode shape");
+    static constexpr int LPS = WI + AI + 1;            // memory instructions per copying wave per stage
+    static constexpr int TNV = TN;
+    __device__ static int frag(int w, int j) { return w / M2 + j * WPM; }
+    __device__ static int mtile(int w) { return w % M2; }
 };
 
 template <int N>
@@ -95,105 +120,128 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Copies of one stage by this wave: its WI pieces of the weight rows, AI pieces of the
-// activation rows and one dword per lane of the scales.
-template <int MT, int TN>
+// Copies of one stage by this wave.  cb/cw: first column and width of the chunk.
+template <class S>
 __device__ __forceinline__ void decode_issue(char *st, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t ar,
-                                             __amdgpu_buffer_rsrc_t sr, int wave, int w_voff,
-                                             const int (&a_voff)[DecodeShape<MT, TN>::AI], int s_voff, int t, int g,
-                                             int N) {
-    using S = DecodeShape<MT, TN>;
+                                             __amdgpu_buffer_rsrc_t sr, int wave, int lane, const int (&a_voff)[S::AI],
+                                             int cb, int cw, int g, int N) {
+    const int last_piece = (cw >> 2) - 1;
 #pragma unroll
     for (int j = 0; j < S::WI; ++j) {
         const int ins = wave * S::WI + j;
-        const uint32_t so = ((uint32_t)(g * 32 + ins * S::RPI) * (uint32_t)N + (uint32_t)(t * TN)) * 4u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + ins * 1024), 16, w_voff, (int)so, 0, kCpolNT);
+        const int p = ins * 64 + lane;
+        const int row = min(p / S::PPR, 31), cp = min(p % S::PPR, last_piece);
+        const int voff = (int)(((uint32_t)row * (uint32_t)N + (uint32_t)(cb + 4 * cp)) * 4u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + ins * 1024), 16, voff,
+                                                 (int)((uint32_t)g * 32u * (uint32_t)N * 4u), 0, kCpolNT);
     }
 #pragma unroll
     for (int j = 0; j < S::AI; ++j) {
         const int ins = wave * S::AI + j;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, I8GS_LDS(st + S::WB + ins * 1024), 16, a_voff[j], g * 128, 0, 0);
     }
-    const uint32_t so = ((uint32_t)g * (uint32_t)N + (uint32_t)(t * TN)) * 4u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, I8GS_LDS(st + S::WB + S::AB + wave * 256), 4, s_voff, (int)so, 0, 0);
+    const int sc = cb + min(wave * 64 + lane, cw - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, I8GS_LDS(st + S::WB + S::AB + wave * 256), 4, sc * 4,
+                                             (int)((uint32_t)g * (uint32_t)N * 4u), 0, 0);
 }
 
-// One stage on the MFMA units: per column quad cc both K steps for every m tile of
-// this wave (int32, exact), then the fold acc += scale * float(group sum).
-template <int MT, int TN>
-__device__ __forceinline__ void decode_compute(const char *st, int slab, int mpart, int li, int lb,
-                                               float (&acc)[4][DecodeShape<MT, TN>::MTW][4]) {
-    using S = DecodeShape<MT, TN>;
-    v4i b[2][4];
+// One stage on the MFMA units: all of this wave's LDS reads for the stage, then the
+// MFMAs of every fragment -- four K steps giving the exact int32 group sums p -- and
+// the fragments' column scales sc.  last_live is false when the wave's last fragment
+// lies past the chunk (then it is skipped).
+template <class S>
+__device__ __forceinline__ void decode_mfma(const char *st, int wave, int lane, bool last_live, v16i (&p)[S::NFW],
+                                            float (&sc)[S::NFW]) {
+    const int col = lane & 31, h = lane >> 5;
+    const int arow = S::mtile(wave) * 32 + col;
+    v4i a[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int ks = 0; ks < 4; ++ks)
+        a[ks] = *reinterpret_cast<const v4i *>(st + S::WB + arow * 128 + (((ks * 2 + h) ^ (arow & 7)) * 16));
+    v4i b[S::NFW][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            b[s][i] = *reinterpret_cast<const v4i *>(st + (16 * s + 4 * lb + i) * (TN * 4) + (slab * 64 + 4 * li) * 4);
-    v4i af[2][S::MTW];
-    const int swz = (li >> 1) & 7;
+    for (int j = 0; j < S::NFW; ++j) {
+        if (j == S::NFW - 1 && !last_live) break;
+        // columns past the chunk read a valid word; their results are never stored
+        const int c = min(S::frag(wave, j) * 32 + col, S::TNV - 1);
+        const int *wcol = reinterpret_cast<const int *>(st) + c;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int m = 0; m < S::MTW; ++m) {
-            const int row = (mpart * S::MTW + m) * 16 + li;
-            af[s][m] = *reinterpret_cast<const v4i *>(st + S::WB + row * 128 + (((s * 4 + lb) ^ swz) * 16));
+            for (int i = 0; i < 4; ++i) b[j][ks][i] = wcol[(8 * ks + 4 * h + i) * (S::PPR * 4)];
+        sc[j] = reinterpret_cast<const float *>(st + S::WB + S::AB)[c];
+    }
+#if I8GS_DECODE_SPLIT_CHAIN
+    // two independent chains of two K steps each, joined by an exact int32 add
+    v16i q[S::NFW];
+#pragma unroll
+    for (int ks = 0; ks < 4; ks += 2)
+#pragma unroll
+        for (int j = 0; j < S::NFW; ++j) {
+            if (j == S::NFW - 1 && !last_live) break;
+            p[j] = mfma32_i8(a[ks], b[j][ks] ^ (int)0x80808080, ks == 0 ? v16i{} : p[j]);
+            q[j] = mfma32_i8(a[ks + 1], b[j][ks + 1] ^ (int)0x80808080, ks == 0 ? v16i{} : q[j]);
         }
-    const v4f sc = *reinterpret_cast<const v4f *>(st + S::WB + S::AB + (slab * 64 + 4 * li) * 4);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-        v4i p[S::MTW];
+    for (int j = 0; j < S::NFW; ++j) {
+        if (j == S::NFW - 1 && !last_live) break;
+        p[j] += q[j];
+    }
+#else
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const v4i bf = v4i{b[s][0][cc], b[s][1][cc], b[s][2][cc], b[s][3][cc]} ^ (int)0x80808080;
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int m = 0; m < S::MTW; ++m) p[m] = mfma_i8(af[s][m], bf, s == 0 ? v4i{0, 0, 0, 0} : p[m]);
+        for (int j = 0; j < S::NFW; ++j) {
+            if (j == S::NFW - 1 && !last_live) break;
+            p[j] = mfma32_i8(a[ks], b[j][ks] ^ (int)0x80808080, ks == 0 ? v16i{} : p[j]);
         }
+#endif
+}
+
+// The fold of one stage: acc += scale * float(group sum).
+template <class S>
+__device__ __forceinline__ void decode_fold(float (&acc)[S::NFW][16], const v16i (&p)[S::NFW],
+                                            const float (&sc)[S::NFW], bool last_live) {
 #pragma unroll
-        for (int m = 0; m < S::MTW; ++m)
+    for (int j = 0; j < S::NFW; ++j) {
+        if (j == S::NFW - 1 && !last_live) break;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[cc][m][r] += sc[cc] * (float)p[m][r];
+        for (int i = 0; i < 16; ++i) acc[j][i] += sc[j] * (float)p[j][i];
     }
 }
 
-// Units of workgroup b when U units are split evenly over P workgroups:
-// [floor(b*U/P), floor((b+1)*U/P)).  The launch keeps P*U below 2^32.
-__device__ __forceinline__ int range_begin(int b, int U, int P) { return (int)((uint32_t)b * (uint32_t)U / (uint32_t)P); }
-__device__ __forceinline__ int owner_of(int u, int U, int P) {
-    return (int)((((uint32_t)u + 1u) * (uint32_t)P - 1u) / (uint32_t)U);
-}
-
-// bf16(a_scale[row] * acc) of this lane's 4 adjacent columns, packed for one 8-byte store.
-__device__ __forceinline__ v2i pack_y(float a, float c0, float c1, float c2, float c3) {
-    return v2i{(int)(f32_to_bf16_bits(a * c0) | ((uint32_t)f32_to_bf16_bits(a * c1) << 16)),
-               (int)(f32_to_bf16_bits(a * c2) | ((uint32_t)f32_to_bf16_bits(a * c3) << 16))};
-}
-
-template <int MT, int TN, int D>
-__global__ __launch_bounds__(256) void w8a8_decode_kernel(const int8_t *__restrict__ qa,
+template <int M2, int TN, int W, int D>
+__global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__restrict__ qa,
                                                           const float *__restrict__ a_scale,
                                                           const int32_t *__restrict__ qweight,
                                                           const float *__restrict__ w_scale,
                                                           uint16_t *__restrict__ y, int64_t ldy, int M, int N, int K,
-                                                          int tiles, int P, float *__restrict__ part) {
-    using S = DecodeShape<MT, TN>;
-    constexpr int MTW = S::MTW;
-    static_assert(D >= 2 && D <= 8 && D * S::STAGE <= 160 * 1024, "LDS ring too large");
+                                                          int T, int S, float *__restrict__ part,
+                                                          int *__restrict__ cnt) {
+    using SH = DecodeShape<M2, TN, W>;
+    constexpr int NFW = SH::NFW;
+    // At least 82 KiB, so that no CU takes two of these workgroups while another has
+    // none (the grid is about one workgroup per CU).
+    constexpr int LDS_BYTES = D * SH::STAGE + 16 > 82 * 1024 ? D * SH::STAGE + 16 : 82 * 1024;
+    static_assert(D >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring too large");
     // One LDS object only: with a second one the compiler can no longer tell the
     // ring's reads from the copies in flight and waits for all of them.
-    __shared__ __attribute__((aligned(1024))) char lds[D * S::STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
-    const int b = blockIdx.x;
-    const int G = K >> 7;
-    const int U = tiles * G;
-    const int u0 = range_begin(b, U, P), u1 = range_begin(b + 1, U, P);
-    if (u0 >= u1) return;
+    const int t = blockIdx.x % T, s = blockIdx.x / T;
+    const int G = K >> 7, NG = N >> 3;
+    const int c0 = 8 * (int)((int64_t)t * NG / T), c1 = 8 * (int)((int64_t)(t + 1) * NG / T);
+    const int g0 = s * G / S, g1 = (s + 1) * G / S;
+    if (c0 >= c1 || g0 >= g1) return;
+    const int wg8 = (c1 - c0) >> 3;           // 8-column granules of the tile
+    const int nch = (c1 - c0 + TN - 1) / TN;  // chunks of at most TN columns
+    const int ng = g1 - g0;
+    const int units = nch * ng;
+
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int slab = wave % S::CQ, mpart = wave / S::CQ;
-    const int li = lane & 15, lb = lane >> 4;
-    const int row0 = mpart * MTW * 16 + 4 * lb;  // this lane's rows: row0 + 16*m + r
-    const int lcol = slab * 64 + 4 * li;         // this lane's 4 columns within a tile
+    const int col = lane & 31, h = lane >> 5;
+    const int row0 = SH::mtile(wave) * 32 + 4 * h;  // this lane's output rows: row0 + 8*(i/4) + i%4
 
     // byte offsets fit 32 bits: K*N < 2^32, M*K < 2^32 and M*ldy*2 < 2^31 are checked
     // before launch
@@ -203,155 +251,191 @@ __global__ __launch_bounds__(256) void w8a8_decode_kernel(const int8_t *__restri
         __builtin_amdgcn_make_buffer_rsrc((void *)qa, 0, (int)((uint32_t)M * (uint32_t)K), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t sr =
         __builtin_amdgcn_make_buffer_rsrc((void *)w_scale, 0, (int)((uint32_t)G * (uint32_t)N * 4u), kRsrcWord3);
-    // Output stores go through a buffer descriptor whose range check drops those
-    // outside y (rows >= M; columns >= N are sent past the end explicitly).
+    // y stores go through a descriptor whose range check drops rows >= M (columns
+    // past the chunk are sent past the end explicitly).
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)y, 0, (int)(((uint32_t)(M - 1) * (uint32_t)ldy + (uint32_t)N) * 2u), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)part, 0, (int)((uint32_t)P * 2u * (uint32_t)(64 * TN * 4)), kRsrcWord3);
 
-    // Per-lane parts of the copy addresses.  Weights: packed row lane / LPR of the
-    // copy, columns 4*(lane % LPR) .. +3.  Activations: LDS slot lane % 8 of row
-    // 8*copy + lane / 8 holds piece slot ^ ((row / 2) % 8) of that row (rows past M
-    // repeat row M - 1; their results are never stored).  Scales: column
-    // (64*wave + lane) % TN.
-    const int w_voff = (lane / S::LPR) * N * 4 + (lane % S::LPR) * 16;
-    int a_voff[S::AI];
+    // Activation copies: LDS slot lane % 8 of row 8*copy + lane / 8 holds piece
+    // slot ^ (row % 8) of that row (rows past M repeat row M - 1; their results are
+    // never stored).
+    const int cwave = wave & 3;                 // copy role (waves 4..7 issue none)
+    const bool copier = W == 4 || wave < 4;
+    int a_voff[SH::AI];
 #pragma unroll
-    for (int j = 0; j < S::AI; ++j) {
-        const int row = (wave * S::AI + j) * 8 + (lane >> 3);
-        const int piece = (lane & 7) ^ ((row >> 1) & 7);
+    for (int j = 0; j < SH::AI; ++j) {
+        const int row = (cwave * SH::AI + j) * 8 + (lane >> 3);
+        const int piece = (lane & 7) ^ (row & 7);
         a_voff[j] = (int)((uint32_t)min(row, M - 1) * (uint32_t)K + (uint32_t)piece * 16u);
     }
-    const int s_voff = ((wave * 64 + lane) % TN) * 4;
 
-    // Row scales of this lane's output rows (4 consecutive rows per m tile; rows past
-    // M read as 0), loaded and waited for before the ring starts: memory operations
-    // complete in order, so a wait for a load issued later would drain the ring.
+    // Row scales of this lane's 16 output rows (rows past M read as 0), loaded and
+    // waited for before the ring starts: memory operations complete in order, so a
+    // wait for a load issued later would drain the ring.
     const __amdgpu_buffer_rsrc_t asr =
         __builtin_amdgcn_make_buffer_rsrc((void *)a_scale, 0, (int)((uint32_t)M * 4u), kRsrcWord3);
-    v4f as[MTW];
+    v4f as[4];  // as[i / 4][i % 4]: rows row0 + 8*(i/4) + i%4
 #pragma unroll
-    for (int m = 0; m < MTW; ++m)
-        as[m] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(asr, (row0 + 16 * m) * 4, 0, 0));
+    for (int q = 0; q < 4; ++q)
+        as[q] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(asr, (row0 + 8 * q) * 4, 0, 0));
 #pragma unroll
-    for (int m = 0; m < MTW; ++m) asm volatile("" ::"v"(as[m]));
+    for (int q = 0; q < 4; ++q) asm volatile("" ::"v"(as[q]));
 
-    int ti = u0 / G, gi = u0 - (u0 / G) * G;  // next unit to copy
+    // Each tile walks its groups starting at a different one, so that the CUs do not
+    // all ask for the same activation group and weight rows at the same moment.
+    const int gstart = g0 + (int)((uint32_t)t * 7u % (uint32_t)ng);
+    // copy cursor: chunk ci (columns [cb, cb + cw)), group gi, step ki within the chunk
+    int ci = 0, gi = gstart, ki = 0;
+    int cb = c0, cw = 8 * (wg8 / nch);
 #pragma unroll
-    for (int s = 0; s < D - 1; ++s) {
-        if (u0 + s < u1) {
-            decode_issue<MT, TN>(lds + s * S::STAGE, wr, ar, sr, wave, w_voff, a_voff, s_voff, ti, gi, N);
-            if (++gi == G) { gi = 0; ++ti; }
+    for (int k = 0; k < D - 1; ++k) {
+        if (k < units) {
+            if (copier) decode_issue<SH>(lds + k * SH::STAGE, wr, ar, sr, cwave, lane, a_voff, cb, cw, gi, N);
+            if (++gi == g1) gi = g0;
+            if (++ki == ng) {
+                ki = 0;
+                ++ci;
+                cb = c0 + 8 * (ci * wg8 / nch);
+                cw = c0 + 8 * ((ci + 1) * wg8 / nch) - cb;
+            }
         }
     }
 
-    const int t_first = u0 / G;
-    int tc = t_first, gc = u0 - t_first * G;  // unit being computed
-    int seg_g0 = gc;                          // first group of the current tile segment
-    float acc[4][MTW][4];
+    // Only a wave's last fragment can lie past the chunk's last fragment.
+    const bool last_live = SH::frag(wave, NFW - 1) < SH::NF;
+    float acc[NFW][16];
+    v16i p_prev[NFW];  // group sums of the previous stage, not yet folded
+    float sc_prev[NFW];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
+    for (int j = 0; j < NFW; ++j) {
+        sc_prev[j] = 0.0f;
+        p_prev[j] = v16i{};
 #pragma unroll
-        for (int m = 0; m < MTW; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[cc][m][r] = 0.0f;
+        for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
+    }
 
+    int kc = 0, kk = 0;  // chunk and step being computed
     int slot = 0;
-    for (int u = u0; u < u1; ++u) {
-        // Memory operations complete in order; the D-2 stages after this one are the
-        // youngest copies, so this count waits for this stage.  Stores issued at the
-        // end of a tile segment are younger still and make this wait longer, not
-        // shorter (counting them exactly, so they stay in flight, measured slower).
-        if (u + D - 2 < u1) wait_vmcnt<(D - 2) * S::LPS>();
+    for (int u = 0; u < units; ++u) {
+        // Memory operations complete in order and the next D-2 stages are the youngest
+        // copies, so this count waits for this stage.  A store issued at the end of a
+        // chunk is younger still and makes the wait longer, not shorter.
+        if (u + D - 2 < units) wait_vmcnt<(D - 2) * SH::LPS>();
         else wait_vmcnt<0>();
         barrier_only();
         __builtin_amdgcn_sched_barrier(0);
-        if (u + D - 1 < u1) {
+        if (u + D - 1 < units) {
             const int ns = slot == 0 ? D - 1 : slot - 1;  // slot of the previous stage, now free
-            decode_issue<MT, TN>(lds + ns * S::STAGE, wr, ar, sr, wave, w_voff, a_voff, s_voff, ti, gi, N);
-            if (++gi == G) { gi = 0; ++ti; }
+            if (copier) decode_issue<SH>(lds + ns * SH::STAGE, wr, ar, sr, cwave, lane, a_voff, cb, cw, gi, N);
+            if (++gi == g1) gi = g0;
+            if (++ki == ng) {
+                ki = 0;
+                ++ci;
+                cb = c0 + 8 * (ci * wg8 / nch);
+                cw = c0 + 8 * ((ci + 1) * wg8 / nch) - cb;
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
-        decode_compute<MT, TN>(lds + slot * S::STAGE, slab, mpart, li, lb, acc);
+        // Software pipeline: this stage's MFMAs run while the previous stage is folded
+        // (zeros at a chunk's first stage: that fold adds exact +0).
+        v16i p_cur[NFW];
+        float sc_cur[NFW];
+        decode_mfma<SH>(lds + slot * SH::STAGE, wave, lane, last_live, p_cur, sc_cur);
+        decode_fold<SH>(acc, p_prev, sc_prev, last_live);
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) {
+            p_prev[j] = p_cur[j];
+            sc_prev[j] = sc_cur[j];
+        }
         slot = slot == D - 1 ? 0 : slot + 1;
 
-        if (gc == G - 1 || u == u1 - 1) {
-            const int col = tc * TN + lcol;
-            if (seg_g0 == 0 && gc == G - 1) {
-                // whole tile: y = bf16(a_scale[row] * sum), 4 columns per store
-                const uint32_t cbase = col < N ? (uint32_t)col * 2u : 0x80000000u;
+        if (++kk < ng) continue;
+        // ---- end of chunk kc
+        decode_fold<SH>(acc, p_prev, sc_prev, last_live);
 #pragma unroll
-                for (int m = 0; m < MTW; ++m)
+        for (int j = 0; j < NFW; ++j) {
+            p_prev[j] = v16i{};
+            sc_prev[j] = 0.0f;
+        }
+        kk = 0;
+        const int kb = c0 + 8 * (kc * wg8 / nch), kw = c0 + 8 * ((kc + 1) * wg8 / nch) - kb;
+        ++kc;
+        if (S == 1) {
+            // y = bf16(a_scale[row] * sum): this lane's column, 16 rows
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const uint32_t off = cbase + (uint32_t)(row0 + 16 * m + r) * (uint32_t)ldy * 2u;
-                        __builtin_amdgcn_raw_buffer_store_b64(
-                            pack_y(as[m][r], acc[0][m][r], acc[1][m][r], acc[2][m][r], acc[3][m][r]), yr,
-                            (int)(col < N ? off : 0x80000000u), 0, 0);
-                    }
-            } else {
-                // piece of a split tile: fp32 [row][TN] in slot 0 (first tile of this
-                // range) or 1 (last tile)
-                const int soff = (b * 2 + (tc == t_first ? 0 : 1)) * (64 * TN * 4);
+            for (int j = 0; j < NFW; ++j) {
+                const int cl = SH::frag(wave, j) * 32 + col;  // column within the chunk
+                const uint32_t cbyte = cl < kw ? (uint32_t)(kb + cl) * 2u : 0x80000000u;
 #pragma unroll
-                for (int m = 0; m < MTW; ++m)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            __builtin_bit_cast(v4i, v4f{acc[0][m][r], acc[1][m][r], acc[2][m][r], acc[3][m][r]}),
-                            pr, ((row0 + 16 * m + r) * TN + lcol) * 4, soff, 0);
+                for (int i = 0; i < 16; ++i) {
+                    const int row = row0 + 8 * (i / 4) + i % 4;
+                    const uint32_t off = cbyte + (uint32_t)row * (uint32_t)ldy * 2u;
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(as[i / 4][i % 4] * acc[j][i]), yr,
+                                                          (int)(cl < kw ? off : 0x80000000u), 0, 0);
+                    acc[j][i] = 0.0f;
+                }
             }
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-                for (int m = 0; m < MTW; ++m)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[cc][m][r] = 0.0f;
-            seg_g0 = 0;
         }
-        if (++gc == G) { gc = 0; ++tc; }
     }
-}
+    if (S == 1) return;
 
-// Sums the pieces of every split tile in workgroup order and writes y.  Block x takes
-// the tile holding the boundary between workgroups x and x + 1 when that boundary lies
-// strictly inside a tile and is the first such boundary of the tile; block y covers
-// 256 (row, 4-column) pieces of it.
-template <int TN>
-__global__ __launch_bounds__(256) void w8a8_splitk_reduce(const float *__restrict__ part,
-                                                          const float *__restrict__ a_scale,
-                                                          uint16_t *__restrict__ y, int64_t ldy, int M, int N,
-                                                          int tiles, int G, int P) {
-    const int U = tiles * G;
-    const int bi = blockIdx.x + 1;
-    const int ub = range_begin(bi, U, P);
-    const int t = ub / G;
-    if (ub == t * G) return;
-    if (bi > 1 && range_begin(bi - 1, U, P) > t * G) return;
-    constexpr int QPR = TN / 4;
-    const int idx = blockIdx.y * 256 + threadIdx.x;
-    const int row = idx / QPR, q = idx % QPR;
-    const int col = t * TN + 4 * q;
-    if (row >= M || col >= N) return;
-    const int bf = owner_of(t * G, U, P), bl = owner_of(t * G + G - 1, U, P);
-    const float *src = part + row * TN + 4 * q;
-    v4f sum;
-    for (int w0 = bf; w0 <= bl; w0 += 8) {
-        // up to 8 pieces in flight at once, summed in workgroup order
-        v4f v[8];
+    // ---- split tile (one chunk): publish this split's piece (fp32 [row][32*NF]; every
+    // fragment lane, also those past the chunk, has its own place; device-coherent),
+    // count arrivals, and let the last split to arrive sum all pieces in split order
+    // (its own from registers: the same values it stored).
+    constexpr int PW = 32 * SH::NF;  // piece row pitch in floats
+    const int piece_bytes = 64 * PW * 4;
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)part, 0, (int)((uint32_t)T * (uint32_t)S * (uint32_t)piece_bytes), kRsrcWord3);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int w = w0 + j;
-            if (w > bl) break;
-            const int sl = range_begin(w, U, P) / G == t ? 0 : 1;
-            v[j] = *reinterpret_cast<const v4f *>(src + (int64_t)(w * 2 + sl) * (64 * TN));
-        }
+    for (int j = 0; j < NFW; ++j) {
+        if (SH::frag(wave, j) >= SH::NF) break;
+        const int cell0 = (row0 * PW + SH::frag(wave, j) * 32 + col) * 4;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (w0 + j <= bl) sum = (w0 + j == bf) ? v[j] : sum + v[j];
+        for (int i = 0; i < 16; ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, acc[j][i]), pr,
+                                                  cell0 + ((8 * (i / 4) + i % 4) * PW) * 4, (s * T + t) * piece_bytes,
+                                                  kCpolSC1);
     }
-    *reinterpret_cast<v2i *>(y + (int64_t)row * ldy + col) = pack_y(a_scale[row], sum[0], sum[1], sum[2], sum[3]);
+    wait_vmcnt<0>();
+    __syncthreads();
+    int *const s_last = reinterpret_cast<int *>(lds + D * SH::STAGE);
+    if (threadIdx.x == 0) {
+        const int last = __hip_atomic_fetch_add(cnt + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+        if (last) __hip_atomic_store(cnt + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = last;
+    }
+    __syncthreads();
+    if (!*s_last) return;
+
+    // The last split sums the pieces in split order, one piece at a time with all of
+    // this lane's cells in flight, and writes y.
+#pragma unroll
+    for (int j = 0; j < NFW; ++j) {
+        if (SH::frag(wave, j) >= SH::NF) break;
+        const int cl = SH::frag(wave, j) * 32 + col;
+        const int cell0 = (row0 * PW + cl) * 4;
+        float sum[16];
+        for (int q = 0; q < S; ++q) {
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                v[i] = q == s ? acc[j][i]
+                              : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                              pr, cell0 + ((8 * (i / 4) + i % 4) * PW) * 4,
+                                                              (q * T + t) * piece_bytes, kCpolSC1));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sum[i] = q == 0 ? v[i] : sum[i] + v[i];
+        }
+        const uint32_t cbyte = (uint32_t)(c0 + cl) * 2u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = row0 + 8 * (i / 4) + i % 4;
+            const uint32_t off = cbyte + (uint32_t)row * (uint32_t)ldy * 2u;
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(as[i / 4][i % 4] * sum[i]), yr,
+                                                  (int)(cl < c1 - c0 ? off : 0x80000000u), 0, 0);
+        }
+    }
 }
 
 int device_cu_count() {
@@ -366,48 +450,79 @@ int device_cu_count() {
     return cached[dev];
 }
 
-#ifndef I8GS_DECODE_TN
-#define I8GS_DECODE_TN 128
-#endif
 #ifndef I8GS_DECODE_STAGES
-#define I8GS_DECODE_STAGES 3
+#define I8GS_DECODE_STAGES 3  // upper bound on the LDS ring's stages
 #endif
 
+// Chunk widths the decode kernel is built for (multiples of 8 columns).
+constexpr int kDecodeTN[] = {32, 48, 64, 80, 96, 128, 144, 192, 256};
+
 struct DecodePlan {
-    int tn;      // tile columns
-    int tiles;   // column tiles
-    int blocks;  // workgroups sharing the (tile, group) units
+    int T, S;  // column tiles x K splits (the grid)
+    int tn;    // chunk width the kernel is built for
+    int m2;    // 32-row m tiles (1 or 2)
 };
 
 DecodePlan decode_plan(int M, int N, int K, int workgroups) {
-    (void)M;
     DecodePlan p;
-    p.tn = I8GS_DECODE_TN;
-    p.tiles = (N + p.tn - 1) / p.tn;
-    const int64_t U = (int64_t)p.tiles * (K / kGroup);
-    int64_t P = workgroups > 0 ? workgroups : (int64_t)device_cu_count();
-    if (P > U) P = U;
-    if (P * U >= (int64_t(1) << 32)) P = ((int64_t(1) << 32) - 1) / U;  // 32-bit range arithmetic
-    if (P < 1) P = 1;
-    p.blocks = (int)P;
+    const int G = K / kGroup, NG = N / 8;
+    const int64_t P = workgroups > 0 ? workgroups : (int64_t)device_cu_count();
+    // K splits so that a tile keeps about 64 columns: S = ceil(64 P / N)
+    int64_t S = (64 * P + N - 1) / N;
+    S = std::max<int64_t>(1, std::min<int64_t>(S, std::min(kMaxSplits, G)));
+    int64_t T = std::max<int64_t>(1, std::min<int64_t>(P / S, NG));
+    if (S > 1 && T > kMaxCounters) T = kMaxCounters;
+    int maxw = 8 * (int)((NG + T - 1) / T);  // widest tile
+    if (S > 1 && maxw > 256) {  // a split tile is one chunk
+        S = 1;
+        T = std::max<int64_t>(1, std::min<int64_t>(P, NG));
+        maxw = 8 * (int)((NG + T - 1) / T);
+    }
+    const int nch = (maxw + 255) / 256;
+    const int chunk = 8 * ((maxw / 8 + nch - 1) / nch);
+    p.tn = 256;
+    for (int tn : kDecodeTN)
+        if (tn >= chunk) { p.tn = tn; break; }
+    p.T = (int)T;
+    p.S = (int)S;
+    p.m2 = M <= 32 ? 1 : 2;
     return p;
 }
 
-// Two fp32 partial tiles (64 rows) per workgroup.
-size_t decode_workspace(const DecodePlan &p) { return align256(size_t(p.blocks) * 2 * 64 * p.tn * sizeof(float)); }
+// One fp32 piece (64 rows x the chunk width rounded up to 32) per workgroup when K
+// is split.
+size_t decode_workspace(const DecodePlan &p) {
+    return p.S > 1 ? align256(size_t(p.T) * p.S * 64 * ((p.tn + 31) / 32 * 32) * sizeof(float)) : 0;
+}
 
-template <int MT, int TN>
-hipError_t launch_decode(const W8A8Args &a, const DecodePlan &p, hipStream_t st) {
-    constexpr int D = I8GS_DECODE_STAGES;
-    float *part = (float *)a.ws;
-    w8a8_decode_kernel<MT, TN, D><<<p.blocks, 256, 0, st>>>(a.qa, a.a_scale, a.qweight, a.w_scale, a.y, a.ldy, a.M,
-                                                             a.N, a.K, p.tiles, p.blocks, part);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.blocks < 2) return e;
-    const dim3 grid(p.blocks - 1, (a.M * (TN / 4) + 255) / 256);
-    w8a8_splitk_reduce<TN><<<grid, 256, 0, st>>>(part, a.a_scale, a.y, a.ldy, a.M, a.N, p.tiles, a.K / kGroup,
-                                                 p.blocks);
+#ifndef I8GS_DECODE_WAVES
+#define I8GS_DECODE_WAVES 8  // two per SIMD, so one wave's latencies hide behind the other's work
+#endif
+
+template <int M2, int TN>
+hipError_t launch_decode_tn(const W8A8Args &a, const DecodePlan &p, hipStream_t st) {
+    constexpr int W = I8GS_DECODE_WAVES;
+    // as many stages as fit in LDS, up to I8GS_DECODE_STAGES
+    constexpr int FIT = (160 * 1024 - 16) / DecodeShape<M2, TN, W>::STAGE;
+    constexpr int D = FIT < I8GS_DECODE_STAGES ? FIT : I8GS_DECODE_STAGES;
+    w8a8_decode_kernel<M2, TN, W, D><<<p.T * p.S, W * 64, 0, st>>>(
+        a.qa, a.a_scale, a.qweight, a.w_scale, a.y, a.ldy, a.M, a.N, a.K, p.T, p.S, (float *)a.ws, a.counters);
     return hipGetLastError();
+}
+
+template <int M2>
+hipError_t launch_decode(const W8A8Args &a, const DecodePlan &p, hipStream_t st) {
+    switch (p.tn) {
+        case 32: return launch_decode_tn<M2, 32>(a, p, st);
+        case 48: return launch_decode_tn<M2, 48>(a, p, st);
+        case 64: return launch_decode_tn<M2, 64>(a, p, st);
+        case 80: return launch_decode_tn<M2, 80>(a, p, st);
+        case 96: return launch_decode_tn<M2, 96>(a, p, st);
+        case 128: return launch_decode_tn<M2, 128>(a, p, st);
+        case 144: return launch_decode_tn<M2, 144>(a, p, st);
+        case 192: return launch_decode_tn<M2, 192>(a, p, st);
+        default: return launch_decode_tn<M2, 256>(a, p, st);
+    }
 }
 
 // ------------------------------------------------------------------ tiled kernel (M > 64)
@@ -538,8 +653,8 @@ size_t w8a8_gemm_workspace(int M, int N, int K, int kernel, int workgroups) {
 hipError_t launch_w8a8_gemm(const W8A8Args &a, hipStream_t s) {
     if (a.P == nullptr && use_decode(a.M, a.kernel) && decode_y_fits(a.M, a.ldy)) {
         const DecodePlan p = decode_plan(a.M, a.N, a.K, a.workgroups);
-        if (a.M <= 32) return launch_decode<2, I8GS_DECODE_TN>(a, p, s);
-        return launch_decode<4, I8GS_DECODE_TN>(a, p, s);
+        if (p.m2 == 1) return launch_decode<1>(a, p, s);
+        return launch_decode<2>(a, p, s);
     }
     dim3 grid((a.N + kTB - 1) / kTB, (a.M + kTB - 1) / kTB);
     if (a.P)

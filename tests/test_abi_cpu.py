@@ -126,6 +126,9 @@ def test_workspace_sizes(lib):
         i8.workspace_bytes(i8.OP_W8A8, 8, 256, 500)
     with pytest.raises(ValueError):
         i8.workspace_bytes(7, 8, 256, 512)
-    # the decode kernel adds two fp32 partial tiles (64 rows x 128 columns) per workgroup
-    assert i8.workspace_bytes(i8.OP_W8A8, 64, 6144, 5120, i8.KERNEL_DECODE, 3) == (
-        65536 + 64 * 5120 + 256 + 3 * 2 * 64 * 128 * 4)
+    # decode kernel, wide layer (no K split): counters and quantised activations only
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 6144, 5120, i8.KERNEL_DECODE, 3) == 65536 + 64 * 5120 + 256
+    # narrow layer: 256 target workgroups on N=512 -> S=8 K parts x T=32 tiles of 16 columns:
+    # one fp32 piece of 64 rows x 32 columns (the chunk width rounded up to 32) per workgroup
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 512, 5120, i8.KERNEL_DECODE, 256) == (
+        65536 + 64 * 5120 + 256 + 32 * 8 * 64 * 32 * 4)
