@@ -6,16 +6,16 @@
 // codes = clamp(rint(x / a_scale), -127, 127), ties to even, with a correctly
 // rounded fp32 division (hipcc's default for '/', no fast-math).
 //
-// One 256-thread workgroup per row.  Each thread keeps its NV 16-byte vectors
-// (8 bf16 each) in registers between the absmax reduction and the quantise step,
-// so the row is read from HBM once; rows longer than 256*8*16 elements take the
-// two-pass variant (NV = 0), whose second read hits L2.
+// One workgroup per row: 1024 threads when there are few rows (decode; more waves
+// per SIMD hide the latency of the load, the reduction and the fp32 divisions),
+// 256 otherwise.  Each thread keeps its NV 16-byte vectors (8 bf16 each) in
+// registers between the absmax reduction and the quantise step, so the row is read
+// once; rows longer than TPB*8*13 elements take the two-pass variant (NV = 0),
+// whose second read hits L2.
 #include "internal.h"
 
 namespace i8gs {
 namespace {
-
-constexpr int kThreads = 256;
 
 __device__ __forceinline__ float absmax8(v4i v, float m) {
 #pragma unroll
@@ -53,6 +53,7 @@ __device__ __forceinline__ v2i quant8(v4i v, float s) {
     return out;
 }
 
+template <int TPB>
 __device__ __forceinline__ float block_max(float m, float *red) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
@@ -61,15 +62,16 @@ __device__ __forceinline__ float block_max(float m, float *red) {
     __syncthreads();
     m = red[0];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
+    for (int w = 1; w < TPB / 64; ++w) m = fmaxf(m, red[w]);
     return m;
 }
 
-template <int NV>
-__global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__restrict__ x, int64_t ldx,
-                                                             int K, int8_t *__restrict__ qa,
-                                                             float *__restrict__ a_scale) {
-    __shared__ float red[kThreads / 64];
+template <int NV, int TPB>
+__global__ __launch_bounds__(TPB) void quant_act_kernel(const uint16_t *__restrict__ x, int64_t ldx,
+                                                        int K, int8_t *__restrict__ qa,
+                                                        float *__restrict__ a_scale) {
+    constexpr int kThreads = TPB;
+    __shared__ float red[TPB / 64];
     const int m = blockIdx.x;
     const int nvec = K >> 3;
     const v4i *row = reinterpret_cast<const v4i *>(x + (int64_t)m * ldx);
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__r
             v[i] = c < nvec ? __builtin_nontemporal_load(row + c) : v4i{0, 0, 0, 0};
             amax = absmax8(v[i], amax);
         }
-        amax = block_max(amax, red);
+        amax = block_max<TPB>(amax, red);
         const float s = amax / 127.0f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
@@ -93,11 +95,33 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__r
         if (threadIdx.x == 0) a_scale[m] = s;
     } else {
         for (int c = threadIdx.x; c < nvec; c += kThreads) amax = absmax8(row[c], amax);
-        amax = block_max(amax, red);
+        amax = block_max<TPB>(amax, red);
         const float s = amax / 127.0f;
         for (int c = threadIdx.x; c < nvec; c += kThreads) out[c] = quant8(row[c], s);
         if (threadIdx.x == 0) a_scale[m] = s;
     }
+}
+
+template <int TPB>
+hipError_t launch_quant_tpb(const uint16_t *x, int64_t ldx, int M, int K, int nvec, int8_t *qa, float *a_scale,
+                            hipStream_t s) {
+    const int per_thread = (nvec + TPB - 1) / TPB;
+    dim3 grid(M), block(TPB);
+    if (per_thread <= 1)
+        quant_act_kernel<1, TPB><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
+    else if (per_thread <= 2)
+        quant_act_kernel<2, TPB><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
+    else if (per_thread <= 3)
+        quant_act_kernel<3, TPB><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
+    else if (per_thread <= 4)
+        quant_act_kernel<4, TPB><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
+    else if (per_thread <= 9)
+        quant_act_kernel<9, TPB><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
+    else if (per_thread <= 13)
+        quant_act_kernel<13, TPB><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
+    else
+        quant_act_kernel<0, TPB><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -105,23 +129,8 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__r
 hipError_t launch_quant_act(const uint16_t *x, int64_t ldx, int M, int K, int8_t *qa, float *a_scale,
                             hipStream_t s) {
     const int nvec = K / 8;
-    const int per_thread = (nvec + kThreads - 1) / kThreads;
-    dim3 grid(M), block(kThreads);
-    if (per_thread <= 1)
-        quant_act_kernel<1><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
-    else if (per_thread <= 2)
-        quant_act_kernel<2><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
-    else if (per_thread <= 3)
-        quant_act_kernel<3><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
-    else if (per_thread <= 4)
-        quant_act_kernel<4><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
-    else if (per_thread <= 9)
-        quant_act_kernel<9><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
-    else if (per_thread <= 13)
-        quant_act_kernel<13><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
-    else
-        quant_act_kernel<0><<<grid, block, 0, s>>>(x, ldx, K, qa, a_scale);
-    return hipGetLastError();
+    if (M <= 512) return launch_quant_tpb<1024>(x, ldx, M, K, nvec, qa, a_scale, s);
+    return launch_quant_tpb<256>(x, ldx, M, K, nvec, qa, a_scale, s);
 }
 
 }  // namespace i8gs

@@ -54,15 +54,15 @@ __device__ __forceinline__ v4i flip(v4i v) {
 // order, so the result does not depend on timing.  The S workgroups of a tile are T
 // apart in launch order.
 //
-// Streaming.  Each workgroup (4 waves; one per CU, the LDS ring takes most of the
-// CU's 160 KiB) pulls its units -- (chunk, group) pairs, chunk-major -- through a
+// Streaming.  Each workgroup (8 waves, two per SIMD; one workgroup per CU, the LDS
+// ring takes most of the CU's 160 KiB) pulls its units -- (chunk, group) pairs, chunk-major -- through a
 // D-stage ring in LDS filled by buffer_load ... lds: a stage holds the chunk's 32
 // packed weight rows of the group (row-major, TN*4 bytes per row), the group's
 // 32*M2 activation rows (128 bytes each) and the chunk's column scales.  The copies
 // go straight from memory to LDS, so D-1 stages stay in flight without holding
-// registers; each wave waits for its own copies of the current stage (vmcnt), a
-// barrier makes all of them visible, and the slot is refilled only after every wave
-// is done with it.  Copies beyond the chunk's columns repeat its last piece (a cache
+// registers; four waves issue the copies, each waits for its own copies of the
+// current stage (vmcnt), a barrier makes all of them visible, and the slot is
+// refilled only after every wave is done with it.  Copies beyond the chunk's columns repeat its last piece (a cache
 // hit), so every wave issues the same number of copies per stage.
 //
 // MFMA.  v_mfma_i32_32x32x32_i8: lane l holds row (l % 32) of A and column (l % 32)
@@ -73,7 +73,7 @@ __device__ __forceinline__ v4i flip(v4i v) {
 // A is the activation rows (m tile of 32 tokens); B is a 32-column fragment of the
 // chunk: lane (col, h) = (l % 32, l / 32) reads, for K step ks, the words of packed
 // rows 8*ks + 4*h + i (i = 0..3) of its column -- 16 consecutive K bytes.  Wave w
-// takes m tile w % 2 and fragments w / 2 + 2j (M > 32), or fragments w + 4j (M <= 32).
+// takes m tile w % M2 and fragments w / M2 + j * (8 / M2).
 // Activations are stored with the 16-byte pieces of row r permuted by XOR with r % 8,
 // so the rows read together fall in different bank groups.
 
@@ -102,7 +102,7 @@ struct DecodeShape {
     static constexpr int WPM = W / M2;                 // waves per m tile
     static constexpr int NFW = (NF + WPM - 1) / WPM;   // fragments per wave
     static constexpr int PPR = TN / 4;                 // 16-byte pieces per weight row
-    // Copies are issued by waves 0..3 (the others only compute).
+    // Copies are issued by four of the waves (the others only compute).
     static constexpr int WI = (TN + 31) / 32;          // 1 KiB weight copies per copying wave per stage
     static constexpr int WB = WI * 4096;               // weight bytes of a stage (TN*128 used)
     static constexpr int AI = M2;                      // 1 KiB activation copies per copying wave
@@ -222,7 +222,9 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
     constexpr int NFW = SH::NFW;
     // At least 82 KiB, so that no CU takes two of these workgroups while another has
     // none (the grid is about one workgroup per CU).
-    constexpr int LDS_BYTES = D * SH::STAGE + 16 > 82 * 1024 ? D * SH::STAGE + 16 : 82 * 1024;
+    // After the ring: the split-arrival flag (16 bytes) and the 64 row scales (256 bytes).
+    constexpr int RING = D * SH::STAGE;
+    constexpr int LDS_BYTES = RING + 512 > 82 * 1024 ? RING + 512 : 82 * 1024;
     static_assert(D >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring too large");
     // One LDS object only: with a second one the compiler can no longer tell the
     // ring's reads from the copies in flight and waits for all of them.
@@ -259,8 +261,10 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
     // Activation copies: LDS slot lane % 8 of row 8*copy + lane / 8 holds piece
     // slot ^ (row % 8) of that row (rows past M repeat row M - 1; their results are
     // never stored).
-    const int cwave = wave & 3;                 // copy role (waves 4..7 issue none)
-    const bool copier = W == 4 || wave < 4;
+    // Copies are issued by the last four waves: with 8 waves, the first ones carry the
+    // extra fragments (frag(w, j) = w / M2 + j * 8 / M2).
+    const int cwave = wave & 3;
+    const bool copier = W == 4 || wave >= 4;
     int a_voff[SH::AI];
 #pragma unroll
     for (int j = 0; j < SH::AI; ++j) {
@@ -269,17 +273,15 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
         a_voff[j] = (int)((uint32_t)min(row, M - 1) * (uint32_t)K + (uint32_t)piece * 16u);
     }
 
-    // Row scales of this lane's 16 output rows (rows past M read as 0), loaded and
-    // waited for before the ring starts: memory operations complete in order, so a
-    // wait for a load issued later would drain the ring.
-    const __amdgpu_buffer_rsrc_t asr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)a_scale, 0, (int)((uint32_t)M * 4u), kRsrcWord3);
-    v4f as[4];  // as[i / 4][i % 4]: rows row0 + 8*(i/4) + i%4
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        as[q] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(asr, (row0 + 8 * q) * 4, 0, 0));
-#pragma unroll
-    for (int q = 0; q < 4; ++q) asm volatile("" ::"v"(as[q]));
+    // The 64 row scales are copied into LDS ahead of the first stage (rows past M read
+    // as 0): the first stage's wait covers this older copy too, and no register load
+    // has to be waited for before the ring starts.
+    float *const lds_as = reinterpret_cast<float *>(lds + RING + 256);
+    if (wave == 0) {
+        const __amdgpu_buffer_rsrc_t asr =
+            __builtin_amdgcn_make_buffer_rsrc((void *)a_scale, 0, (int)((uint32_t)M * 4u), kRsrcWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(asr, I8GS_LDS(lds_as), 4, lane * 4, 0, 0, 0);
+    }
 
     // Each tile walks its groups starting at a different one, so that the CUs do not
     // all ask for the same activation group and weight rows at the same moment.
@@ -362,6 +364,9 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
         ++kc;
         if (S == 1) {
             // y = bf16(a_scale[row] * sum): this lane's column, 16 rows
+            v4f as[4];  // as[i / 4][i % 4]: row row0 + 8*(i/4) + i%4
+#pragma unroll
+            for (int q = 0; q < 4; ++q) as[q] = *reinterpret_cast<const v4f *>(lds_as + row0 + 8 * q);
 #pragma unroll
             for (int j = 0; j < NFW; ++j) {
                 const int cl = SH::frag(wave, j) * 32 + col;  // column within the chunk
@@ -399,7 +404,7 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
     }
     wait_vmcnt<0>();
     __syncthreads();
-    int *const s_last = reinterpret_cast<int *>(lds + D * SH::STAGE);
+    int *const s_last = reinterpret_cast<int *>(lds + RING);
     if (threadIdx.x == 0) {
         const int last = __hip_atomic_fetch_add(cnt + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
         if (last) __hip_atomic_store(cnt + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -408,31 +413,54 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
     __syncthreads();
     if (!*s_last) return;
 
-    // The last split sums the pieces in split order, one piece at a time with all of
-    // this lane's cells in flight, and writes y.
+    // The last split sums the pieces in split order: the other splits' cells are
+    // loaded QB pieces at a time, all in flight together, and its own come from
+    // registers (the same values it stored).
+    constexpr int QB = NFW > 1 ? 2 : 4;
+    v4f as[4];  // as[i / 4][i % 4]: row row0 + 8*(i/4) + i%4
+#pragma unroll
+    for (int q = 0; q < 4; ++q) as[q] = *reinterpret_cast<const v4f *>(lds_as + row0 + 8 * q);
+    float sum[NFW][16];
+    for (int q0 = 0; q0 < S; q0 += QB) {
+        float v[QB][NFW][16];
+#pragma unroll
+        for (int k = 0; k < QB; ++k) {
+            const int q = q0 + k;
+            if (q >= S) break;
+#pragma unroll
+            for (int j = 0; j < NFW; ++j) {
+                if (SH::frag(wave, j) >= SH::NF) break;
+                const int cell0 = (row0 * PW + SH::frag(wave, j) * 32 + col) * 4;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    v[k][j][i] = q == s ? acc[j][i]
+                                        : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                        pr, cell0 + ((8 * (i / 4) + i % 4) * PW) * 4,
+                                                                        (q * T + t) * piece_bytes, kCpolSC1));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < QB; ++k) {
+            const int q = q0 + k;
+            if (q >= S) break;
+#pragma unroll
+            for (int j = 0; j < NFW; ++j) {
+                if (SH::frag(wave, j) >= SH::NF) break;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sum[j][i] = q == 0 ? v[k][j][i] : sum[j][i] + v[k][j][i];
+            }
+        }
+    }
 #pragma unroll
     for (int j = 0; j < NFW; ++j) {
         if (SH::frag(wave, j) >= SH::NF) break;
         const int cl = SH::frag(wave, j) * 32 + col;
-        const int cell0 = (row0 * PW + cl) * 4;
-        float sum[16];
-        for (int q = 0; q < S; ++q) {
-            float v[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                v[i] = q == s ? acc[j][i]
-                              : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                              pr, cell0 + ((8 * (i / 4) + i % 4) * PW) * 4,
-                                                              (q * T + t) * piece_bytes, kCpolSC1));
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sum[i] = q == 0 ? v[i] : sum[i] + v[i];
-        }
         const uint32_t cbyte = (uint32_t)(c0 + cl) * 2u;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int row = row0 + 8 * (i / 4) + i % 4;
             const uint32_t off = cbyte + (uint32_t)row * (uint32_t)ldy * 2u;
-            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(as[i / 4][i % 4] * sum[i]), yr,
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(as[i / 4][i % 4] * sum[j][i]), yr,
                                                   (int)(cl < c1 - c0 ? off : 0x80000000u), 0, 0);
         }
     }
