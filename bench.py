@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="skip prefill and W4A16 figures")
     ap.add_argument("--lm-head", action="store_true", help="also time the 248320-column INT8 vocabulary head")
     ap.add_argument("--min-cold-bytes", type=float, default=1.0e9)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="no timing: 4 decode steps plus a 256 MiB device copy (the calibration kernel), for "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
     return ap.parse_args()
 
 
@@ -102,8 +105,8 @@ def spin(torch, ms):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); run it with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (sharding is a "
+              "design note only); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -139,6 +142,25 @@ def main():
     log(f"inputs ready in {time.time() - t0:.1f}s: {nsets} weight sets of {set_bytes / 1e6:.1f} MB")
 
     timer = Timer(torch)
+
+    if args.traffic_probe:
+        # Counter runs: a plain copy of known size first (its FETCH_SIZE / WRITE_SIZE give
+        # the counters' scale), then 4 decode steps in layer order qkv, o_proj, gate_up, down.
+        copy_bytes = 256 << 20
+        src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        for i in range(4):
+            ws = wsets[i % nsets]
+            for li, L in enumerate(layers):
+                qw, sc = ws[li]
+                i8.gemm_w8a8_g128(qw, sc, qa=qas[li], a_scale=scs[li], y=ys[li])
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": True, "copy_bytes": copy_bytes,
+                          "gemm_bytes": {L.name: gemm_bytes(M, L.K, L.N) for L in layers}}), flush=True)
+        return
 
     def step(i, timed):
         ws = wsets[i % nsets]

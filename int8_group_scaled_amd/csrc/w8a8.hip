@@ -51,8 +51,7 @@ __device__ __forceinline__ v4i flip(v4i v) {
 // layers take S > 1 so that a tile stays about 64 columns wide or more (each streamed
 // weight byte then costs at most one activation byte); the S workgroups of a tile
 // each write an fp32 piece and the last of them to finish sums the pieces in split
-// order, so the result does not depend on timing.  The S workgroups of a tile are T
-// apart in launch order.
+// order, so the result does not depend on timing.
 //
 // Streaming.  Each workgroup (8 waves, two per SIMD; one workgroup per CU, the LDS
 // ring takes most of the CU's 160 KiB) pulls its units -- (chunk, group) pairs, chunk-major -- through a
@@ -230,7 +229,15 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
     // ring's reads from the copies in flight and waits for all of them.
     __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
-    const int t = blockIdx.x % T, s = blockIdx.x / T;
+    // XCD-aware placement: workgroups are dealt to the 8 XCDs round-robin by launch
+    // index, so logical workgroup L (tile-major: L = t*S + s) is launched at index
+    // (L % Q) * 8 + L / Q with Q = ceil(P/8).  Each XCD then holds a contiguous run
+    // of tiles: neighbouring tiles share the cache lines at their borders in one L2,
+    // and the S splits of a tile meet in one L2 too.  (Only speed depends on this.)
+    const int P = T * S, Q = (P + 7) >> 3;
+    const int L = (blockIdx.x & 7) * Q + (blockIdx.x >> 3);
+    if (L >= P) return;
+    const int t = L / S, s = L - (L / S) * S;
     const int G = K >> 7, NG = N >> 3;
     const int c0 = 8 * (int)((int64_t)t * NG / T), c1 = 8 * (int)((int64_t)(t + 1) * NG / T);
     const int g0 = s * G / S, g1 = (s + 1) * G / S;
@@ -283,9 +290,9 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
         __builtin_amdgcn_raw_ptr_buffer_load_lds(asr, I8GS_LDS(lds_as), 4, lane * 4, 0, 0, 0);
     }
 
-    // Each tile walks its groups starting at a different one, so that the CUs do not
-    // all ask for the same activation group and weight rows at the same moment.
-    const int gstart = g0 + (int)((uint32_t)t * 7u % (uint32_t)ng);
+    // All tiles walk their groups in the same order, so neighbouring tiles read the
+    // cache lines they share at about the same time.
+    const int gstart = g0;
     // copy cursor: chunk ci (columns [cb, cb + cw)), group gi, step ki within the chunk
     int ci = 0, gi = gstart, ki = 0;
     int cb = c0, cw = 8 * (wg8 / nch);
@@ -533,7 +540,7 @@ hipError_t launch_decode_tn(const W8A8Args &a, const DecodePlan &p, hipStream_t 
     // as many stages as fit in LDS, up to I8GS_DECODE_STAGES
     constexpr int FIT = (160 * 1024 - 16) / DecodeShape<M2, TN, W>::STAGE;
     constexpr int D = FIT < I8GS_DECODE_STAGES ? FIT : I8GS_DECODE_STAGES;
-    w8a8_decode_kernel<M2, TN, W, D><<<p.T * p.S, W * 64, 0, st>>>(
+    w8a8_decode_kernel<M2, TN, W, D><<<(p.T * p.S + 7) / 8 * 8, W * 64, 0, st>>>(
         a.qa, a.a_scale, a.qweight, a.w_scale, a.y, a.ldy, a.M, a.N, a.K, p.T, p.S, (float *)a.ws, a.counters);
     return hipGetLastError();
 }
