@@ -25,7 +25,8 @@
  *    y[m,n]     = bf16( a_scale[m] * sum_g w_scale[g,n] * P[m,g,n] )
  *  The group sums are exact; the fold over groups is fp32 in any order, so y is
  *  within one bf16 unit of the exact value plus (K/128 + 2) * 2^-24 times
- *  a_scale[m] * sum_g |w_scale[g,n] * P[m,g,n]|.
+ *  a_scale[m] * sum_g |w_scale[g,n] * P[m,g,n]|.  Scales are finite with
+ *  |w_scale| < 2^100 (the decode kernel folds with w_scale * 2^26).
  *
  * Layouts (all row-major, little-endian):
  *  x        bf16   [M, ldx]        activations (ldx >= K, ldx % 8 == 0)
@@ -79,9 +80,10 @@ typedef enum {
 #define I8GS_OP_W4A16 1
 
 /* Kernel choice for gemm_w8a8_g128_ex(). */
-#define I8GS_KERNEL_AUTO 0   /* decode kernel for M <= 64, tiled kernel otherwise */
+#define I8GS_KERNEL_AUTO 0   /* decode kernel for M <= 64, the 256x256-tile prefill kernel
+                                otherwise (the 128x128 tiled kernel when M*ldy*2 >= 2^31) */
 #define I8GS_KERNEL_DECODE 1 /* weight-streaming kernel (M <= 64 only) */
-#define I8GS_KERNEL_TILED 2  /* LDS-tiled MFMA kernel, any M */
+#define I8GS_KERNEL_TILED 2  /* 128x128 LDS-tiled MFMA kernel, any M */
 
 /* ABI version of the loaded library (I8GS_ABI_VERSION at build time). */
 int i8gs_abi_version(void);
@@ -146,9 +148,9 @@ int gemm_w8a8_g128(const void *x, int64_t ldx, const int8_t *qa, const float *a_
  * kernel splits the columns into T tiles of multiples of 8 columns and, for narrow
  * layers, K into S <= 8 parts of whole 128-wide groups (S = ceil(64 * target / N),
  * T = target / S, both clamped to the layer), so it runs T*S workgroups.  Every
- * choice computes the same exact group sums; only the fp32 fold order differs.  I8GS_KERNEL_DECODE is rejected when M > 64 or
- * when M*ldy*2 >= 2^31 (32-bit output offsets); I8GS_KERNEL_AUTO takes the tiled
- * kernel in that case.
+ * choice computes the same exact group sums; only the fp32 fold order differs.
+ * I8GS_KERNEL_DECODE is rejected when M > 64 or when M*ldy*2 >= 2^31 (32-bit
+ * output offsets); I8GS_KERNEL_AUTO takes the 128x128 tiled kernel in that case.
  */
 int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float *a_scale,
                       const int32_t *qweight, const float *w_scale, void *y, int64_t ldy, int64_t M,

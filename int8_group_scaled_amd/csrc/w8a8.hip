@@ -93,6 +93,31 @@ __device__ __forceinline__ v16i mfma32_i8(v4i a, v4i b, v16i c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
+// Group sums leave the MFMA already shaped for a cheap fold.  A group's MFMA chain starts
+// from the accumulator value kSumSeed (the fp32 bit pattern of 1/(2*pi), an inline
+// constant of the MFMA's C operand) instead of 0.  Read as an fp32 number, the int32
+// result kSumSeed + S equals f_seed + S * 2^-26 exactly while it stays in the seed's
+// binade [1/8, 1/4), i.e. for -2291075 <= S <= 6097532, and a sum of 128 products of
+// two int8 values lies within +-2097152.  f_seed minus that number is then exact
+// (Sterbenz): -S * 2^-26 for one full-rate VALU op with an inline constant, where an
+// int-to-float convert costs a half-rate one, and multiplying it by -scale * 2^26
+// gives exactly the product scale * S that the fold adds.  (Scales must keep
+// scale * 2^26 finite: |scale| < 2^100.)
+constexpr int kSumSeed = 0x3E22F983;
+constexpr float kSumScale = -67108864.0f;  // -2^26
+
+__device__ __forceinline__ v16i sum_seed() {
+    v16i c;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = kSumSeed;
+    return c;
+}
+
+// -S * 2^-26 from a seeded group sum (exact).
+__device__ __forceinline__ float seeded_sum(int r) {
+    return __builtin_bit_cast(float, kSumSeed) - __builtin_bit_cast(float, r);
+}
+
 template <int M2, int TN, int W>
 struct DecodeShape {
     static_assert((M2 == 1 || M2 == 2) && (W == 4 || W == 8) && TN % 8 == 0 && TN >= 8 && TN <= 256,
@@ -145,8 +170,8 @@ __device__ __forceinline__ void decode_issue(char *st, __amdgpu_buffer_rsrc_t wr
 }
 
 // One stage on the MFMA units: all of this wave's LDS reads for the stage, then the
-// MFMAs of every fragment -- four K steps giving the exact int32 group sums p -- and
-// the fragments' column scales sc.  last_live is false when the wave's last fragment
+// MFMAs of every fragment -- four K steps giving the exact int32 group sums p, seeded
+// (see sum_seed) -- and the fragments' column scales sc, times -2^26.  last_live is false when the wave's last fragment
 // lies past the chunk (then it is skipped).
 template <class S>
 __device__ __forceinline__ void decode_mfma(const char *st, int wave, int lane, bool last_live, v16i (&p)[S::NFW],
@@ -168,7 +193,7 @@ __device__ __forceinline__ void decode_mfma(const char *st, int wave, int lane, 
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int i = 0; i < 4; ++i) b[j][ks][i] = wcol[(8 * ks + 4 * h + i) * (S::PPR * 4)];
-        sc[j] = reinterpret_cast<const float *>(st + S::WB + S::AB)[c];
+        sc[j] = reinterpret_cast<const float *>(st + S::WB + S::AB)[c] * kSumScale;
     }
 #if I8GS_DECODE_SPLIT_CHAIN
     // two independent chains of two K steps each, joined by an exact int32 add
@@ -178,7 +203,7 @@ __device__ __forceinline__ void decode_mfma(const char *st, int wave, int lane, 
 #pragma unroll
         for (int j = 0; j < S::NFW; ++j) {
             if (j == S::NFW - 1 && !last_live) break;
-            p[j] = mfma32_i8(a[ks], b[j][ks] ^ (int)0x80808080, ks == 0 ? v16i{} : p[j]);
+            p[j] = mfma32_i8(a[ks], b[j][ks] ^ (int)0x80808080, ks == 0 ? sum_seed() : p[j]);
             q[j] = mfma32_i8(a[ks + 1], b[j][ks + 1] ^ (int)0x80808080, ks == 0 ? v16i{} : q[j]);
         }
 #pragma unroll
@@ -192,12 +217,13 @@ __device__ __forceinline__ void decode_mfma(const char *st, int wave, int lane, 
 #pragma unroll
         for (int j = 0; j < S::NFW; ++j) {
             if (j == S::NFW - 1 && !last_live) break;
-            p[j] = mfma32_i8(a[ks], b[j][ks] ^ (int)0x80808080, ks == 0 ? v16i{} : p[j]);
+            p[j] = mfma32_i8(a[ks], b[j][ks] ^ (int)0x80808080, ks == 0 ? sum_seed() : p[j]);
         }
 #endif
 }
 
-// The fold of one stage: acc += scale * float(group sum).
+// The fold of one stage: acc += scale * group sum (sc holds scale * -2^26, p the seeded
+// sums; a zero p with a zero sc adds an exact 0).
 template <class S>
 __device__ __forceinline__ void decode_fold(float (&acc)[S::NFW][16], const v16i (&p)[S::NFW],
                                             const float (&sc)[S::NFW], bool last_live) {
@@ -205,7 +231,7 @@ __device__ __forceinline__ void decode_fold(float (&acc)[S::NFW][16], const v16i
     for (int j = 0; j < S::NFW; ++j) {
         if (j == S::NFW - 1 && !last_live) break;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[j][i] += sc[j] * (float)p[j][i];
+        for (int i = 0; i < 16; ++i) acc[j][i] += sc[j] * seeded_sum(p[j][i]);
     }
 }
 
@@ -560,7 +586,190 @@ hipError_t launch_decode(const W8A8Args &a, const DecodePlan &p, hipStream_t st)
     }
 }
 
-// ------------------------------------------------------------------ tiled kernel (M > 64)
+// ------------------------------------------------------------------ prefill kernel (M > 64)
+//
+// Bound by the MFMA units and, as much, by the VALU: folding a 32x32 int32 group sum
+// into fp32 takes a convert and an FMA per value, 32 wave-wide VALU ops per lane that
+// cost as many cycles as the tile's four MFMAs.  A workgroup (8 waves, one per CU: its
+// LDS takes 130 KiB) owns a 256 x 256 output tile and walks the K groups with a
+// 2-stage LDS ring filled by buffer_load ... lds: a stage holds the group's 256
+// activation rows (128 bytes, pieces XOR-swizzled by row % 8), the 32 packed weight
+// rows of the tile's 256 columns (rows 4..7 of every 8 shifted by 8 pieces, so the two
+// lane halves of a B read hit different banks) and their scales.  The next stage's
+// copies are issued right after the barrier that frees its slot, so they run under the
+// current stage's MFMAs.
+//
+// Wave w owns rows 128*(w / 4) .. +127 and columns 64*(w % 4) .. +63 of the tile:
+// 4 m tiles x 2 column fragments of 32x32.  Per group it reads its B fragments (the
+// words of packed rows 8*ks + 4*h + i of its column, as in the decode kernel) and, one
+// m tile ahead, its A fragments.  Two waves per SIMD let one wave's folds run under
+// the other's MFMAs.
+
+constexpr int kPB = 256;                      // prefill tile rows and columns
+constexpr int kPStageA = kPB * 128;           // activation bytes of a stage
+constexpr int kPStageB = 32 * kPB * 4;        // weight bytes of a stage
+constexpr int kPStage = kPStageA + kPStageB + kPB * 4;
+
+__global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restrict__ qa,
+                                                           const float *__restrict__ a_scale,
+                                                           const int32_t *__restrict__ qweight,
+                                                           const float *__restrict__ w_scale,
+                                                           uint16_t *__restrict__ y, int64_t ldy, int M, int N,
+                                                           int K) {
+    __shared__ __attribute__((aligned(1024))) char lds[2 * kPStage];
+    const int mtiles = (M + kPB - 1) / kPB, ntiles = (N + kPB - 1) / kPB;
+    // XCD-aware placement (see the decode kernel): logical tile L = nt * mtiles + mt, so
+    // the m tiles of one column tile -- which read the same weights -- share an XCD.
+    const int P = mtiles * ntiles, Q = (P + 7) >> 3;
+    const int L = (blockIdx.x & 7) * Q + (blockIdx.x >> 3);
+    if (L >= P) return;
+    const int mt = L % mtiles, nt = L / mtiles;
+    const int m0 = mt * kPB, n0 = nt * kPB;
+    const int G = K >> 7;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 31, h = lane >> 5;
+    const int wm = wave >> 2, wn = wave & 3;
+
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)qweight, 0, (int)((uint32_t)K * (uint32_t)N), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ar =
+        __builtin_amdgcn_make_buffer_rsrc((void *)qa, 0, (int)((uint32_t)M * (uint32_t)K), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t sr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)w_scale, 0, (int)((uint32_t)G * (uint32_t)N * 4u), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)y, 0, (int)(((uint32_t)(M - 1) * (uint32_t)ldy + (uint32_t)N) * 2u), kRsrcWord3);
+
+    // Copy roles: 32 activation copies (8 rows each) and 32 weight copies (half a
+    // packed row each) per stage, 4 + 4 per wave, plus the 256 scales (waves 0..3).
+    // LDS slot p of the 32 x 256 weight block holds row p / 64, piece (p % 64) ^ swz(row):
+    // rows 4..7 of every 8 are shifted by 8 pieces (32 words), so the two halves of a
+    // wave, which read rows 4 apart, use different banks.  A wave's four weight rows
+    // 4*wave .. +3 share the swizzle, so one lane offset serves them all.
+    int a_voff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = (wave * 4 + j) * 8 + (lane >> 3);
+        const int piece = (lane & 7) ^ (row & 7);
+        a_voff[j] = (int)((uint32_t)min(m0 + row, M - 1) * (uint32_t)K + (uint32_t)piece * 16u);
+    }
+    const int cp = min(n0 + (lane ^ (wave & 1 ? 8 : 0)) * 4, N - 4);
+    const int w_voff = (int)(((uint32_t)(wave * 4) * (uint32_t)N + (uint32_t)cp) * 4u);
+    const int s_voff = min(n0 + (wave & 3) * 64 + lane, N - 1) * 4;
+
+    auto issue = [&](char *st, int g) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, I8GS_LDS(st + (wave * 4 + j) * 1024), 16, a_voff[j], g * 128,
+                                                     0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + kPStageA + (wave * 4 + j) * 1024), 16, w_voff,
+                                                     (int)(((uint32_t)g * 32u + (uint32_t)j) * (uint32_t)N * 4u), 0, 0);
+        if (wave < 4)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, I8GS_LDS(st + kPStageA + kPStageB + wave * 256), 4, s_voff,
+                                                     (int)((uint32_t)g * (uint32_t)N * 4u), 0, 0);
+    };
+
+    float acc[4][2][16];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][f][i] = 0.0f;
+
+    // The fold here converts the plain int32 sums (v_cvt_f32_i32): measured a little
+    // faster in this kernel than the seeded form the decode kernel uses.
+    v16i pp = {};     // the chain folded under the next one and its scale (zero: adds an exact 0)
+    float scp = 0.0f;
+    issue(lds, 0);
+    for (int g = 0; g < G; ++g) {
+        char *st = lds + (g & 1) * kPStage;
+        wait_vmcnt<0>();
+        barrier_only();  // this stage is in; every wave is done with the other slot
+        __builtin_amdgcn_sched_barrier(0);
+        if (g + 1 < G) issue(lds + ((g + 1) & 1) * kPStage, g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // B fragments of this wave's two 32-column fragments, offset binary -> int8.  Lane
+        // half h reads rows 8*ks + 4*h + i, whose pieces are swizzled by 8*h.
+        v4i b[2][4];
+        float sc[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const int c = wn * 64 + f * 32 + col;
+            const int cs = c ^ (h ? 32 : 0);
+            const int *wcol = reinterpret_cast<const int *>(st + kPStageA) + cs;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) b[f][ks][i] = wcol[(8 * ks + 4 * h + i) * kPB];
+            sc[f] = reinterpret_cast<const float *>(st + kPStageA + kPStageB)[c];
+        }
+        // Eight chains per group, chain c = (m tile c / 2, fragment c % 2): four dependent
+        // MFMAs (the exact int32 group sum of one 32x32 tile), then the fold of chain
+        // c - 1 into its fp32 accumulator (the last chain of a group is folded after the
+        // first chain of the next), so the fold's VALU work has no MFMA result to wait
+        // for and runs beside the MFMAs of this wave and of the other wave on the SIMD.
+        // A fragments are read one m tile ahead.
+        v4i a[4], an[4];
+        {
+            const int arow = wm * 128 + col;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                a[ks] = *reinterpret_cast<const v4i *>(st + arow * 128 + (((ks * 2 + h) ^ (arow & 7)) * 16));
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int mi = c >> 1, f = c & 1;
+            if (f == 0 && mi < 3) {
+                const int arow = wm * 128 + (mi + 1) * 32 + col;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    an[ks] = *reinterpret_cast<const v4i *>(st + arow * 128 + (((ks * 2 + h) ^ (arow & 7)) * 16));
+            }
+            v16i p;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) p = mfma32_i8(a[ks], b[f][ks] ^ (int)0x80808080, ks == 0 ? v16i{} : p);
+            const int pm = c == 0 ? 3 : (c - 1) >> 1, pf = c == 0 ? 1 : (c - 1) & 1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[pm][pf][i] += scp * (float)pp[i];
+            pp = p;
+            scp = sc[f];
+            if (f == 1) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) a[ks] = an[ks];
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[3][1][i] += scp * (float)pp[i];
+
+    // y = bf16(a_scale[row] * acc): lane (col, h) holds column n0 + 64*wn + 32*f + col,
+    // rows m0 + 128*wm + 32*mi + 8*(i/4) + 4*h + i%4.
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int rbase = m0 + wm * 128 + mi * 32 + 4 * h;
+        float as[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) as[i] = a_scale[min(rbase + 8 * (i / 4) + i % 4, M - 1)];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const int cn = n0 + wn * 64 + f * 32 + col;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = rbase + 8 * (i / 4) + i % 4;
+                const uint32_t off = ((uint32_t)row * (uint32_t)ldy + (uint32_t)cn) * 2u;
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(as[i] * acc[mi][f][i]), yr,
+                                                      (int)(cn < N ? off : 0x80000000u), 0, 0);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ tiled kernel (group partials; M > 64 fallback)
 
 constexpr int kTB = 128;       // tile rows and columns
 constexpr int kPitch = 144;    // LDS row pitch in bytes (128 + 16)
@@ -690,6 +899,12 @@ hipError_t launch_w8a8_gemm(const W8A8Args &a, hipStream_t s) {
         const DecodePlan p = decode_plan(a.M, a.N, a.K, a.workgroups);
         if (p.m2 == 1) return launch_decode<1>(a, p, s);
         return launch_decode<2>(a, p, s);
+    }
+    if (a.P == nullptr && a.kernel != I8GS_KERNEL_TILED && decode_y_fits(a.M, a.ldy)) {
+        const int tiles = ((a.M + kPB - 1) / kPB) * ((a.N + kPB - 1) / kPB);
+        w8a8_prefill_kernel<<<(tiles + 7) / 8 * 8, 512, 0, s>>>(a.qa, a.a_scale, a.qweight, a.w_scale, a.y, a.ldy,
+                                                                 a.M, a.N, a.K);
+        return hipGetLastError();
     }
     dim3 grid((a.N + kTB - 1) / kTB, (a.M + kTB - 1) / kTB);
     if (a.P)

@@ -105,6 +105,19 @@ def test_decode_and_tiled_kernels_agree_with_oracle():
         assert_within_tolerance(host_bf16_bits(y), y_exact, T, K, what=f"kernel {kern}")
 
 
+@pytest.mark.parametrize("M,K,N", [(600, 640, 520), (257, 256, 264), (512, 1280, 768)])
+def test_prefill_and_tiled_kernels_multi_tile(M, K, N):
+    """M > 64: the 256x256 prefill kernel (auto) and the 128x128 tiled kernel, over
+    several tiles with ragged last rows and columns, against the oracle."""
+    xb, qw, ws = _case(4, f"pf{M}-{K}-{N}", M, K, N, True)
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, oracle.gptq_unpack(qw, 8, K), ws)
+    for kern in (i8.KERNEL_AUTO, i8.KERNEL_TILED):
+        y = i8.gemm_w8a8_g128_ex(dev(qw), dev(ws), qa=dev(qa), a_scale=dev(s), kernel=kern)
+        torch.cuda.synchronize()
+        assert_within_tolerance(host_bf16_bits(y), y_exact, T, K, what=f"kernel {kern} {M}x{K}x{N}")
+
+
 def test_identity_probe_recovers_dequantised_rows():
     """Running an identity matrix through the layer returns the dense dequantised
     weight rows (the W8A8-W8A16 drafter card's identity probe): row m is e_m, so
