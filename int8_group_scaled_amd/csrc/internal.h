@@ -68,7 +68,28 @@ struct W4A16Args {
     size_t ws_bytes;
 };
 size_t w4a16_gemm_workspace(int M, int N, int K);
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cu_count();
 hipError_t launch_w4a16_gemm(const W4A16Args &a, hipStream_t s);
+
+// Buffer resource word 3 (raw buffer, gfx9-family format) and cache-policy bits.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kCpolNT = 2;    // non-temporal: streamed data is not reused
+constexpr int kCpolSC1 = 16;  // device-coherent (across the XCDs' L2 caches)
+
+// LDS pointer for buffer_load ... lds copies.
+#define I8GS_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// Workgroup barrier without the fence of __syncthreads (which would also wait for
+// every copy in flight); the compiler keeps memory accesses on their side of it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// Wait until at most N of this wave's memory operations are outstanding (they
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

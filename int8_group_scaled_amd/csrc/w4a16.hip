@@ -5,12 +5,13 @@
 // linears and fc in INT4 g128 sym).  y[m,n] = bf16(sum_g w_scale[g,n] *
 // sum_{k in g} x[m,k] * q[k,n]) with q = nibble - 8.
 //
-// Each nibble is turned into the exact bf16 value of q (an integer in [-8, 7]:
-// XOR 8 makes it a two's-complement 4-bit field, a signed bit-field extract and
-// an int->float conversion give q exactly, and the top half of that float is its
-// bf16 pattern).  One 128-wide group is summed by four v_mfma_f32_16x16x32_bf16
-// into a fresh fp32 accumulator (the products are exact in fp32), then scaled by
-// that group's per-column scale and added to the running fp32 sum.  Scaling after
+// Each nibble is turned into the exact bf16 value of 16*q (q an integer in [-8, 7]):
+// masking a word's high nibbles in place, or its low nibbles shifted up by 4, and
+// flipping bit 7 of every byte leaves 16*q as a signed byte; a sign-extending byte
+// convert (SDWA) gives the fp32 value, whose top half is its bf16 pattern.  One
+// 128-wide group is summed by four v_mfma_f32_16x16x32_bf16 into a fresh fp32
+// accumulator (the products are exact in fp32), then scaled by that group's
+// per-column scale / 16 (exact) and added to the running fp32 sum.  Scaling after
 // the group keeps the error relative to sum |x*q| rather than to the cancelling
 // scaled terms.
 //
@@ -18,32 +19,36 @@
 // of B, 8 consecutive K values starting at 8 * (l / 16) within the 32-wide K step;
 // with GPTQ's packing those 8 values of one column are exactly one int32 word.
 //
-// At decode sizes the bf16 activation rows are the larger operand (2 bytes per
-// element against half a byte of weight), so a workgroup stages each group's
-// activations in LDS once and its W waves, each owning F 16-column fragments,
-// all read them; weight words go straight from HBM into registers, one group
-// ahead.  K is split across S workgroups when the column tiles alone cannot fill
-// the GPU, with the same deterministic last-arrival reduction as the W8A8 path.
-// Rows are processed in chunks of 64 (gridDim.y).
+// Data flow (as in the W8A8 decode kernel): a workgroup of 8 waves owns a tile of
+// 128 columns (16 per wave) and up to 64 rows, and walks its K groups through a
+// D-stage LDS ring filled by buffer_load ... lds copies -- a stage holds the group's
+// 16 packed weight rows of the tile, its activation rows (bf16, 256 bytes each) and
+// the tile's scales -- with the wait for a stage issued D - 2 stages behind the
+// copies, so D - 1 groups are in flight.  K is split across S workgroups when the
+// column tiles alone cannot fill the GPU; the splits publish fp32 partials with
+// device-coherent stores and the last to arrive sums them in split order.  Rows
+// are processed in chunks of 64 (gridDim.y).
 #include "internal.h"
 
 namespace i8gs {
 namespace {
 
-constexpr int kMC = 64;           // rows per chunk
-constexpr int kAPitch = 128 + 8;  // bf16 elements per LDS row (272 bytes)
+constexpr int kMC = 64;  // rows per chunk
+constexpr int kTN = 128;  // columns per tile (16 per wave)
 
-__device__ __forceinline__ v8bf dequant8(uint32_t w) {
-    const uint32_t s = w ^ 0x88888888u;
-    uint32_t h[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int q = ((int)(s << (28 - 4 * j))) >> 28;  // signed nibble j: code - 8
-        h[j] = __float_as_uint((float)q);
-    }
+// The 8 codes of one word as bf16 of 16*q, in K order.  Byte i of the word holds
+// codes 2i (low nibble) and 2i+1 (high nibble); (code ^ 8) is q as a 4-bit two's-
+// complement field, so a byte holding it in its high nibble reads as 16*q.
+__device__ __forceinline__ v8bf dequant8x16(uint32_t w) {
+    const uint32_t odd = (w & 0xF0F0F0F0u) ^ 0x80808080u;
+    const uint32_t even = ((w << 4) & 0xF0F0F0F0u) ^ 0x80808080u;
     v4i out;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = (int)((h[2 * i] >> 16) | (h[2 * i + 1] & 0xFFFF0000u));
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t fe = __float_as_uint((float)(signed char)(even >> (8 * i)));
+        const uint32_t fo = __float_as_uint((float)(signed char)(odd >> (8 * i)));
+        out[i] = (int)((fe >> 16) | (fo & 0xFFFF0000u));
+    }
     return __builtin_bit_cast(v8bf, out);
 }
 
@@ -51,177 +56,214 @@ __device__ __forceinline__ v4f mfma_bf16(v4i a, v8bf b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), b, c, 0, 0, 0);
 }
 
-template <int MT, int F, int W>
-__global__ __launch_bounds__(W * 64) void w4a16_decode_kernel(
+// Stage layout (bytes): the 16 x 128 weight words, row-major, with the 16-byte pieces
+// of packed row r permuted by XOR with 4 * (r % 4) (a B read's four lane groups read
+// rows 4 apart: they land in different banks); then the activation rows, 256 bytes
+// each, pieces permuted by XOR with row % 16; then the 128 scales.
+template <int MT>
+struct W4Stage {
+    static constexpr int ROWS = 16 * MT;
+    static constexpr int WB = 16 * kTN * 4;
+    static constexpr int AB = ROWS * 256;
+    static constexpr int SB = kTN * 4;
+    static constexpr int BYTES = WB + AB + SB;
+    static constexpr int ACOPIES = AB / 1024;              // 1 KiB activation copies per stage
+    static constexpr int AI = (ACOPIES + 7) / 8;           // per wave (extra ones repeat the last)
+    static constexpr int LPS = 1 + AI + 1;                 // copies per wave per stage
+};
+
+// The copies of one stage (group g) by this wave.
+template <int MT>
+__device__ __forceinline__ void w4_issue(char *st, int g, int wave, int N, __amdgpu_buffer_rsrc_t wr,
+                                         __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t sr, int w_voff,
+                                         const int (&a_voff)[W4Stage<MT>::AI], const int (&a_ins)[W4Stage<MT>::AI],
+                                         int s_half, int s_voff) {
+    using SG = W4Stage<MT>;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + wave * 1024), 16, w_voff,
+                                             (int)((uint32_t)g * 16u * (uint32_t)N * 4u), 0, kCpolNT);
+#pragma unroll
+    for (int j = 0; j < SG::AI; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, I8GS_LDS(st + SG::WB + a_ins[j] * 1024), 16, a_voff[j], g * 256,
+                                                 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, I8GS_LDS(st + SG::WB + SG::AB + s_half * 256), 4, s_voff,
+                                             (int)((uint32_t)g * (uint32_t)N * 4u), 0, 0);
+}
+
+template <int MT, int D>
+__global__ __launch_bounds__(512) void w4a16_stream_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, const int32_t *__restrict__ qweight,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ldy, int M, int N, int K, int S,
-    int tiles, float *__restrict__ part, int *__restrict__ cnt) {
-    constexpr int TN = 16 * F * W;
-    constexpr int ROWS = MT * 16;
-    constexpr int CHUNKS = ROWS * 16 / (W * 64);  // 16-byte A pieces per thread per group
-    static_assert(CHUNKS >= 1 && CHUNKS * W * 64 == ROWS * 16, "A staging must divide evenly");
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][ROWS * kAPitch];
+    int tiles, float *__restrict__ part, size_t part_bytes, int *__restrict__ cnt) {
+    using SG = W4Stage<MT>;
+    constexpr int RING = D * SG::BYTES;
+    // One LDS object only (see the W8A8 decode kernel); the split flag sits after the ring.
+    __shared__ __attribute__((aligned(1024))) char lds[RING + 16];
 
-    const int per_xcd = gridDim.x >> 3;
-    const int pair = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    if (pair >= tiles * S) return;
-    const int t = pair / S;
-    const int s = pair - t * S;
+    // XCD-aware placement: logical workgroup L (tile-major) at launch index (L % Q) * 8 + L / Q.
+    const int P = tiles * S, Q = (P + 7) >> 3;
+    const int L = (blockIdx.x & 7) * Q + (blockIdx.x >> 3);
+    if (L >= P) return;
+    const int t = L / S, s = L - (L / S) * S;
     const int m0 = blockIdx.y * kMC;
-    const int mrows = min(M - m0, ROWS);
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int li = lane & 15, lb = lane >> 4;
-    const int n0 = t * TN + wave * 16 * F;
+    const int mrows = min(M - m0, SG::ROWS);
+    const int n0 = t * kTN;
     const int G = K >> 7;
     const int g0 = (int)((int64_t)s * G / S), g1 = (int)((int64_t)(s + 1) * G / S);
+    const int ng = g1 - g0;
 
-    int bcol[F];
-#pragma unroll
-    for (int f = 0; f < F; ++f) bcol[f] = min(n0 + f * 16 + li, N - 1);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int li = lane & 15, lb = lane >> 4;
 
-    // A staging: piece c = tid + i * W*64 covers row c / 16, 16 bytes at (c % 16) * 8 elements.
-    const uint16_t *arow_ptr[CHUNKS];
-    int aoff[CHUNKS];
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-        const int c = tid + i * W * 64;
-        const int row = c >> 4, col = (c & 15) * 8;
-        arow_ptr[i] = x + (int64_t)(m0 + min(row, mrows - 1)) * ldx + col;
-        aoff[i] = row * kAPitch + col;
+    // byte offsets fit 32 bits: K*N < 2^32 is checked before launch, and x is
+    // addressed from this chunk's first row
+    const uint16_t *xc = x + (int64_t)m0 * ldx;
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)qweight, 0, (int)((uint32_t)K / 8u * (uint32_t)N * 4u), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)xc, 0, (int)(((uint32_t)(mrows - 1) * (uint32_t)ldx + (uint32_t)K) * 2u), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t sr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)w_scale, 0, (int)((uint32_t)G * (uint32_t)N * 4u), kRsrcWord3);
+
+    // Copy roles (every wave issues LPS copies per stage, so one wait count serves all).
+    // Weights: wave w fills packed rows 2w, 2w+1 (32 pieces of 4 columns each).
+    int w_voff;
+    {
+        const int r = 2 * wave + (lane >> 5), sl = lane & 31;
+        const int piece = sl ^ ((r & 3) << 2);
+        w_voff = (int)(((uint32_t)r * (uint32_t)N + (uint32_t)min(n0 + 4 * piece, N - 4)) * 4u);
     }
-
-    float acc[F][MT][4];
+    // Activations: copy c fills rows 4c .. 4c+3 (16 pieces each); rows past the chunk
+    // repeat its last row (never stored).
+    int a_voff[SG::AI], a_ins[SG::AI];
 #pragma unroll
-    for (int f = 0; f < F; ++f)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[f][mt][r] = 0.0f;
-
-    v4i areg[CHUNKS];
-    int wq[F][4];
-    if (g0 < g1) {
-#pragma unroll
-        for (int i = 0; i < CHUNKS; ++i) areg[i] = *reinterpret_cast<const v4i *>(arow_ptr[i] + g0 * 128);
-#pragma unroll
-        for (int f = 0; f < F; ++f)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                wq[f][ks] = __builtin_nontemporal_load(qweight + (int64_t)(g0 * 16 + ks * 4 + lb) * N + bcol[f]);
+    for (int j = 0; j < SG::AI; ++j) {
+        a_ins[j] = min(wave * SG::AI + j, SG::ACOPIES - 1);
+        const int row = 4 * a_ins[j] + (lane >> 4), sl = lane & 15;
+        const int piece = sl ^ (row & 15);
+        a_voff[j] = (int)(((uint32_t)min(row, mrows - 1) * (uint32_t)ldx + (uint32_t)piece * 8u) * 2u);
     }
-    for (int g = g0; g < g1; ++g) {
-        const int buf = (g - g0) & 1;
-        uint16_t *Ab = As[buf];
-#pragma unroll
-        for (int i = 0; i < CHUNKS; ++i) *reinterpret_cast<v4i *>(Ab + aoff[i]) = areg[i];
-        int wc[F][4];
-#pragma unroll
-        for (int f = 0; f < F; ++f)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) wc[f][ks] = wq[f][ks];
-        if (g + 1 < g1) {
-#pragma unroll
-            for (int i = 0; i < CHUNKS; ++i) areg[i] = *reinterpret_cast<const v4i *>(arow_ptr[i] + (g + 1) * 128);
-#pragma unroll
-            for (int f = 0; f < F; ++f)
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    wq[f][ks] =
-                        __builtin_nontemporal_load(qweight + (int64_t)((g + 1) * 16 + ks * 4 + lb) * N + bcol[f]);
-        }
-        __syncthreads();
-        float sc[F];
-#pragma unroll
-        for (int f = 0; f < F; ++f) sc[f] = w_scale[(int64_t)g * N + bcol[f]];
-        v4f p[F][MT];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            v4i a[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                a[mt] = *reinterpret_cast<const v4i *>(Ab + (mt * 16 + li) * kAPitch + ks * 32 + lb * 8);
-#pragma unroll
-            for (int f = 0; f < F; ++f) {
-                const v8bf b = dequant8((uint32_t)wc[f][ks]);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    p[f][mt] = mfma_bf16(a[mt], b, ks == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : p[f][mt]);
-            }
-        }
-#pragma unroll
-        for (int f = 0; f < F; ++f)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[f][mt][r] += sc[f] * p[f][mt][r];
-    }
+    // Scales: half k = wave % 2 of the tile's 128 (waves 2..7 repeat them).
+    const int s_half = wave & 1;
+    const int s_voff = min(n0 + 64 * s_half + lane, N - 1) * 4;
 
-    if (S > 1) {
-        constexpr int NACC = F * MT * 4;
-        const int64_t tile_id = (int64_t)blockIdx.y * tiles + t;
-        float *mine = part + ((tile_id * S + s) * W + wave) * NACC * 64;
-        {
-            int i = 0;
-#pragma unroll
-            for (int f = 0; f < F; ++f)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r, ++i) mine[i * 64 + lane] = acc[f][mt][r];
-        }
-        __threadfence();
-        __syncthreads();
-        __shared__ int s_old;
-        if (tid == 0) s_old = atomicAdd(cnt + tile_id, 1);
-        __syncthreads();
-        if (s_old != S - 1) return;
-        __threadfence();
-        int i = 0;
-#pragma unroll
-        for (int f = 0; f < F; ++f)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r, ++i) {
-                    float v = 0.0f;
-                    for (int q = 0; q < S; ++q)
-                        v += __builtin_nontemporal_load(part + (((tile_id * S + q) * W + wave) * NACC + i) * 64 + lane);
-                    acc[f][mt][r] = v;
-                }
-        if (tid == 0) cnt[tile_id] = 0;
-    }
-
+    float acc[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = mt * 16 + lb * 4 + r;
-            if (row < mrows) {
+        for (int r = 0; r < 4; ++r) acc[mt][r] = 0.0f;
+
 #pragma unroll
-                for (int f = 0; f < F; ++f) {
-                    const int col = n0 + f * 16 + li;
-                    if (col < N) y[(int64_t)(m0 + row) * ldy + col] = f32_to_bf16_bits(acc[f][mt][r]);
-                }
+    for (int k = 0; k < D - 1; ++k)
+        if (k < ng) w4_issue<MT>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, sr, w_voff, a_voff, a_ins, s_half, s_voff);
+
+    // This lane's B words: column 16*wave + li of packed rows 4*ks + lb.
+    const int cl = 16 * wave + li;
+    int b_off[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int r = 4 * ks + lb;
+        b_off[ks] = (r * kTN + (((cl >> 2) ^ ((r & 3) << 2)) << 2) + (cl & 3)) * 4;
+    }
+    int slot = 0;
+    for (int u = 0; u < ng; ++u) {
+        // Copies complete in issue order and the next D-2 stages are the youngest ones.
+        if (u + D - 2 < ng) wait_vmcnt<(D - 2) * SG::LPS>();
+        else wait_vmcnt<0>();
+        barrier_only();  // this stage is in; every wave is done with the previous slot
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + D - 1 < ng)
+            w4_issue<MT>(lds + (slot == 0 ? D - 1 : slot - 1) * SG::BYTES, g0 + u + D - 1, wave, N, wr, xr, sr, w_voff,
+                         a_voff, a_ins, s_half, s_voff);
+        __builtin_amdgcn_sched_barrier(0);
+        const char *st = lds + slot * SG::BYTES;
+        v4f p[MT];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const v8bf b = dequant8x16((uint32_t)*reinterpret_cast<const int *>(st + b_off[ks]));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int row = mt * 16 + li;
+                const v4i a = *reinterpret_cast<const v4i *>(st + SG::WB + row * 256 + (((4 * ks + lb) ^ li) << 4));
+                p[mt] = mfma_bf16(a, b, ks == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : p[mt]);
             }
         }
+        const float sc = reinterpret_cast<const float *>(st + SG::WB + SG::AB)[cl] * 0.0625f;  // sums are 16x
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[mt][r] += sc * p[mt][r];
+        slot = slot == D - 1 ? 0 : slot + 1;
+    }
+
+    if (S > 1) {
+        // Partial of split q, wave w: MT*4 fp32 cells of 64 lanes at
+        // ((tile * S + q) * 8 + w) * MT*4 * 64 (device-coherent stores and loads: the
+        // splits may run on different XCDs).
+        constexpr int NACC = MT * 4;
+        const int tile_id = blockIdx.y * tiles + t;
+        const __amdgpu_buffer_rsrc_t pr =
+            __builtin_amdgcn_make_buffer_rsrc((void *)part, 0, (int)part_bytes, kRsrcWord3);
+        const uint32_t qstride = 8u * NACC * 64 * 4;
+        const uint32_t cell0 = (uint32_t)tile_id * (uint32_t)S * qstride + ((uint32_t)wave * NACC * 64 + lane) * 4u;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(acc[mt][r]), pr,
+                                                      (int)(cell0 + (uint32_t)(mt * 4 + r) * 256u),
+                                                      (int)((uint32_t)s * qstride), kCpolSC1);
+        wait_vmcnt<0>();
+        __syncthreads();
+        int *const s_last = reinterpret_cast<int *>(lds + RING);
+        if (threadIdx.x == 0) {
+            const int last =
+                __hip_atomic_fetch_add(cnt + tile_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+            if (last) __hip_atomic_store(cnt + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *s_last = last;
+        }
+        __syncthreads();
+        if (!*s_last) return;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = 0.0f;
+                for (int q = 0; q < S; ++q) {
+                    const float c = q == s ? acc[mt][r]
+                                           : __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                                 pr, (int)(cell0 + (uint32_t)(mt * 4 + r) * 256u),
+                                                 (int)((uint32_t)q * qstride), kCpolSC1));
+                    v = q == 0 ? c : v + c;
+                }
+                acc[mt][r] = v;
+            }
+    }
+
+    const int col = n0 + cl;
+    if (col < N) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = mt * 16 + lb * 4 + r;
+                if (row < mrows) y[(int64_t)(m0 + row) * ldy + col] = f32_to_bf16_bits(acc[mt][r]);
+            }
+    }
 }
 
 struct W4Plan {
-    int MT, F, W, S, tiles, blocks, chunks;
+    int MT, S, tiles, blocks, chunks;
 };
 
 W4Plan w4_plan(int M, int N, int K) {
     W4Plan p;
     p.MT = M >= 64 ? 4 : (M + 15) / 16;
-    p.F = 2;
-    p.W = 4;
     p.chunks = (M + kMC - 1) / kMC;
-    const int TN = 16 * p.F * p.W;
-    p.tiles = (N + TN - 1) / TN;
+    p.tiles = (N + kTN - 1) / kTN;
     const int G = K / kGroup;
-    int S = (256 + p.tiles * p.chunks - 1) / (p.tiles * p.chunks);
+    const int P = device_cu_count();
+    int S = (P + p.tiles * p.chunks - 1) / (p.tiles * p.chunks);
     if (S > G) S = G;
     if (S < 1) S = 1;
     if (p.tiles * p.chunks > kMaxCounters) S = 1;
@@ -230,13 +272,16 @@ W4Plan w4_plan(int M, int N, int K) {
     return p;
 }
 
-template <int MT>
+// As many stages as fit in 80 KiB (two workgroups per CU), at most 6.
+template <int MT, int D>
 hipError_t launch_w4_mt(const W4A16Args &a, const W4Plan &p, hipStream_t st) {
+    static_assert(D * W4Stage<MT>::BYTES + 16 <= 80 * 1024 && (D == 6 || (D + 1) * W4Stage<MT>::BYTES + 16 > 80 * 1024),
+                  "stage count must be the largest that fits 80 KiB");
     int *cnt = p.S > 1 ? a.counters : nullptr;
     float *part = p.S > 1 ? (float *)a.ws : nullptr;
     dim3 grid(p.blocks, p.chunks);
-    w4a16_decode_kernel<MT, 2, 4><<<grid, 256, 0, st>>>(a.x, a.ldx, a.qweight, a.w_scale, a.y, a.ldy, a.M, a.N,
-                                                       a.K, p.S, p.tiles, part, cnt);
+    w4a16_stream_kernel<MT, D><<<grid, 512, 0, st>>>(a.x, a.ldx, a.qweight, a.w_scale, a.y, a.ldy, a.M, a.N, a.K,
+                                                    p.S, p.tiles, part, p.S > 1 ? a.ws_bytes : 0, cnt);
     return hipGetLastError();
 }
 
@@ -246,16 +291,16 @@ hipError_t launch_w4_mt(const W4A16Args &a, const W4Plan &p, hipStream_t st) {
 size_t w4a16_gemm_workspace(int M, int N, int K) {
     const W4Plan p = w4_plan(M, N, K);
     if (p.S <= 1) return 0;
-    return align256(size_t(p.tiles) * p.chunks * p.S * p.W * p.F * p.MT * 4 * 64 * sizeof(float));
+    return align256(size_t(p.tiles) * p.chunks * p.S * 8 * p.MT * 4 * 64 * sizeof(float));
 }
 
 hipError_t launch_w4a16_gemm(const W4A16Args &a, hipStream_t s) {
     const W4Plan p = w4_plan(a.M, a.N, a.K);
     switch (p.MT) {
-        case 1: return launch_w4_mt<1>(a, p, s);
-        case 2: return launch_w4_mt<2>(a, p, s);
-        case 3: return launch_w4_mt<3>(a, p, s);
-        default: return launch_w4_mt<4>(a, p, s);
+        case 1: return launch_w4_mt<1, 6>(a, p, s);
+        case 2: return launch_w4_mt<2, 4>(a, p, s);
+        case 3: return launch_w4_mt<3, 3>(a, p, s);
+        default: return launch_w4_mt<4, 3>(a, p, s);
     }
 }
 

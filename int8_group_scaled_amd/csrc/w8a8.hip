@@ -33,10 +33,6 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Workgroup barrier without the fence of __syncthreads (which would also wait for
-// every copy in flight); the compiler keeps memory accesses on their side of it.
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
-
 __device__ __forceinline__ v4i flip(v4i v) {
     return v ^ (int)0x80808080;
 }
@@ -76,11 +72,7 @@ __device__ __forceinline__ v4i flip(v4i v) {
 // Activations are stored with the 16-byte pieces of row r permuted by XOR with r % 8,
 // so the rows read together fall in different bank groups.
 
-#define I8GS_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9-family format word
-constexpr int kCpolNT = 2;             // non-temporal: streamed weights are not reused
-constexpr int kCpolSC1 = 16;           // device-coherent (across the XCDs' L2 caches)
 constexpr int kMaxSplits = 8;
 
 #ifndef I8GS_DECODE_SPLIT_CHAIN
@@ -139,10 +131,6 @@ struct DecodeShape {
     __device__ static int mtile(int w) { return w % M2; }
 };
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // Copies of one stage by this wave.  cb/cw: first column and width of the chunk.
 template <class S>
@@ -499,17 +487,6 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
     }
 }
 
-int device_cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
 
 #ifndef I8GS_DECODE_STAGES
 #define I8GS_DECODE_STAGES 3  // upper bound on the LDS ring's stages
@@ -879,6 +856,19 @@ __global__ __launch_bounds__(256) void w8a8_tiled_kernel(const int8_t *__restric
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 static bool use_decode(int M, int kernel) {
     if (kernel == I8GS_KERNEL_DECODE) return true;
