@@ -14,12 +14,15 @@ Timing: W untimed steps, then exactly K steps between two synchronisations.
 Before the K steps a short spin kernel is queued so the host can enqueue all of
 them ahead of the GPU; the step time is then the GPU time between HIP events
 recorded on the launch stream before the first and after the last step, and the
-per-kernel durations come from events around every launch on that stream.
+per-kernel durations come from events around every launch of every 8th timed
+step on that stream (an event between two kernels adds a gap of its own).
 
 value = algorithmic bytes of the step / step time, with per-layer bytes
 K*N (codes) + 4*N*K/128 (fp32 scales) + 2*M*K (bf16 x) + 2*M*N (bf16 y).
 The roofline entry is for the GEMM kernel: bytes per launch K*N + 4*N*K/128 +
-M*K + 4*M (qa, a_scale) + 2*M*N, over its average duration, against 8 TB/s.
+M*K + 4*M (qa, a_scale) + 2*M*N, over its average duration, against 8 TB/s;
+`traffic` is the HBM bytes per launch measured with rocprofv3 counters (see
+DECODE_TRAFFIC), null when the kernel sources have changed since.
 Secondary figures: prefill (4096 tokens, five layers, GEMM kernel on
 pre-quantised activations) in TOP/s against the 5.0 POP/s dense INT8 peak, the
 W4A16 g128 sibling on the decode shapes, and the CPU oracle on the host cores.
@@ -40,6 +43,20 @@ sys.path.insert(0, ROOT)
 
 METRIC = "W8A8-G128 GEMM: GB/s at decode M=64 + INT8 TOPS at prefill M=4096, % peak"
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per launch of the decode GEMM kernel on the four layers, from two
+# rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over `bench.py --traffic-probe`,
+# each counter scaled by its own reading for the probe's 256 MiB device copy
+# (FETCH_SIZE counts half the bytes read: x2.0; WRITE_SIZE: x1.0).  The figures hold
+# for the kernel sources they were taken with, identified by the SHA-256 of
+# DECODE_SOURCES; after any change to those files `traffic` is reported as null.
+DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h", "include/i8gs.h")
+DECODE_TRAFFIC = {
+    "sources_sha256": "7a2c5bd6920bf6c79366c55a818bdd695344541db43e837f685def1a2f844065",
+    "fetch": {"qkv": 40426368, "o_proj": 28620542, "gate_up": 192603831, "down": 106202076},
+    "write": {"qkv": 7070336, "o_proj": 6957056, "gate_up": 4456488, "down": 6957056},
+}
+EVENT_EVERY = 8  # per-kernel HIP events on every 8th timed step (each event adds a gap)
 INT8_PEAK_TOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -62,6 +79,15 @@ def parse():
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def decode_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def gemm_bytes(M, K, N):
@@ -185,7 +211,7 @@ def main():
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(args.steps):
-        step(args.warmup + i, True)
+        step(args.warmup + i, i % EVENT_EVERY == 0)
     end.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
@@ -205,6 +231,12 @@ def main():
                              "gemm_frac_hbm": round(b / (gm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     achieved = g_bytes / (g_us * 1e-6) / 1e9
     log(f"decode step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s; GEMM kernels {achieved:.0f} GB/s")
+    traffic = None
+    if decode_sources_sha256() == DECODE_TRAFFIC["sources_sha256"]:
+        traffic = round(sum(DECODE_TRAFFIC["fetch"][L.name] + DECODE_TRAFFIC["write"][L.name] for L in layers)
+                        / len(layers))
+    else:
+        log("decode kernel sources differ from those the traffic counters were taken with: traffic = null")
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -217,8 +249,10 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "w8a8_decode_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "bytes_per_launch": "K*N + 4*N*K/128 + M*K + 4*M + 2*M*N (sum over the 4 layers: %d)" % int(g_bytes),
+                     "traffic": traffic,
+                     "traffic_unit": "bytes per launch (mean of the 4 layers; FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
+                     "bytes_per_launch": "K*N + 4*N*K/128 + M*K + 4*M + 2*M*N (mean of the 4 layers: %d)"
+                                         % int(g_bytes / len(layers)),
                      "avg_launch_us": round(g_us / len(layers), 3)},
         "per_layer": per_layer,
     }
@@ -263,7 +297,7 @@ def main():
             torch.cuda.empty_cache()
         tops = tot_ops / (tot_us * 1e-6) / 1e12
         out["prefill"] = {"M": Mp, "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
-                          "kernel": "w8a8_tiled_kernel", "per_layer": pre}
+                          "kernel": "w8a8_prefill_kernel", "per_layer": pre}
         log(f"prefill GEMMs {tops:.0f} TOP/s ({tops / INT8_PEAK_TOPS:.1%} of dense INT8 peak)")
 
         # ---------------- W4A16 g128 on the decode shapes (secondary)
