@@ -47,7 +47,7 @@ __device__ __forceinline__ v8bf dequant8x16(uint32_t w) {
     for (int i = 0; i < 4; ++i) {
         const uint32_t fe = __float_as_uint((float)(signed char)(even >> (8 * i)));
         const uint32_t fo = __float_as_uint((float)(signed char)(odd >> (8 * i)));
-        out[i] = (int)((fe >> 16) | (fo & 0xFFFF0000u));
+        out[i] = (int)__builtin_amdgcn_perm(fo, fe, 0x07060302u);  // top halves: (fe >> 16) | (fo & 0xFFFF0000)
     }
     return __builtin_bit_cast(v8bf, out);
 }
@@ -224,20 +224,31 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
         }
         __syncthreads();
         if (!*s_last) return;
+        // Sum in split order; the other splits' cells are loaded QB splits at a time, all
+        // in flight together (this split's own come from registers: the values it stored).
+        constexpr int QB = MT > 2 ? 2 : 4;
+        float sum[NACC];
+        for (int q0 = 0; q0 < S; q0 += QB) {
+            float v[QB][NACC];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int k = 0; k < QB; ++k) {
+                const int q = min(q0 + k, S - 1);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float v = 0.0f;
-                for (int q = 0; q < S; ++q) {
-                    const float c = q == s ? acc[mt][r]
-                                           : __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                                 pr, (int)(cell0 + (uint32_t)(mt * 4 + r) * 256u),
-                                                 (int)((uint32_t)q * qstride), kCpolSC1));
-                    v = q == 0 ? c : v + c;
-                }
-                acc[mt][r] = v;
+                for (int i = 0; i < NACC; ++i)
+                    v[k][i] = q == s ? acc[i / 4][i % 4]
+                                     : __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                           pr, (int)(cell0 + (uint32_t)i * 256u), (int)((uint32_t)q * qstride),
+                                           kCpolSC1));
             }
+#pragma unroll
+            for (int k = 0; k < QB; ++k) {
+                if (q0 + k >= S) break;
+#pragma unroll
+                for (int i = 0; i < NACC; ++i) sum[i] = q0 + k == 0 ? v[k][i] : sum[i] + v[k][i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) acc[i / 4][i % 4] = sum[i];
     }
 
     const int col = n0 + cl;
