@@ -516,6 +516,22 @@ DecodePlan decode_plan(int M, int N, int K, int workgroups) {
         T = std::max<int64_t>(1, std::min<int64_t>(P, NG));
         maxw = 8 * (int)((NG + T - 1) / T);
     }
+    // Narrow layers: tiles of whole 32-column fragments work best (measured on the drafter
+    // layers).  128-column tiles give every wave exactly one fragment x m tile per group,
+    // so they win when each split still has at least 16 groups to stream; otherwise
+    // 64-column tiles with at least 8 groups per split, else the split above.
+    if (S > 1) {
+        for (const int w : {128, 64}) {
+            const int64_t Tw = (N + w - 1) / w;
+            const int64_t Sw = std::min<int64_t>(std::min<int64_t>(kMaxSplits, G), P / Tw);
+            if (Sw >= 2 && Tw <= kMaxCounters && G >= (w == 128 ? 16 : 8) * Sw) {
+                T = Tw;
+                S = Sw;
+                maxw = 8 * (int)((NG + T - 1) / T);
+                break;
+            }
+        }
+    }
     const int nch = (maxw + 255) / 256;
     const int chunk = 8 * ((maxw / 8 + nch - 1) / nch);
     p.tn = 256;
