@@ -52,9 +52,9 @@ HBM_PEAK_GBS = 8000.0
 # DECODE_SOURCES; after any change to those files `traffic` is reported as null.
 DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h", "include/i8gs.h")
 DECODE_TRAFFIC = {
-    "sources_sha256": "7a2c5bd6920bf6c79366c55a818bdd695344541db43e837f685def1a2f844065",
-    "fetch": {"qkv": 40426368, "o_proj": 28620542, "gate_up": 192603831, "down": 106202076},
-    "write": {"qkv": 7070336, "o_proj": 6957056, "gate_up": 4456488, "down": 6957056},
+    "sources_sha256": "722fb171ef74a871b01a8f7bde095c110d6c0d20a83f32ef26ccb5af58ef26b5",
+    "fetch": {"qkv": 36814744, "o_proj": 26529676, "gate_up": 192015071, "down": 107593727},
+    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456448, "down": 8528640},
 }
 EVENT_EVERY = 8  # per-kernel HIP events on every 8th timed step (each event adds a gap)
 INT8_PEAK_TOPS = 5000.0
