@@ -46,3 +46,20 @@ def test_w4a16_repeatable():
     b = i8.gemm_w4a16_g128(dev_bf16(xb), dev(qw), dev(ws))
     torch.cuda.synchronize()
     assert np.array_equal(host_bf16_bits(a), host_bf16_bits(b))
+
+
+@pytest.mark.parametrize("M,K,N", [(8, 640, 264), (64, 1280, 392), (70, 384, 136)])
+def test_w4a16_strided_rows(M, K, N):
+    """x and y addressed with row strides larger than K and N (ldx = K + 64, ldy = N + 24):
+    the padding columns of y stay untouched."""
+    xb = synth.activations_bf16(3, f"w4s{M}-{K}-{N}", M, K, outliers=True)
+    qw, ws = rtn_weights(3, f"w4s{M}-{K}-{N}", K, N, 4)
+    xfull = torch.zeros((M, K + 64), dtype=torch.bfloat16, device="cuda")
+    xfull[:, :K] = dev_bf16(xb)
+    yfull = torch.full((M, N + 24), 7.0, dtype=torch.bfloat16, device="cuda")
+    i8.gemm_w4a16_g128(xfull[:, :K], dev(qw), dev(ws), y=yfull[:, :N])
+    torch.cuda.synchronize()
+    y_exact, T = oracle.gemm_w4a16_g128(xb, unpacked(3, f"w4s{M}-{K}-{N}", K, N, 4), ws)
+    assert_within_tolerance(host_bf16_bits(yfull[:, :N].contiguous()), y_exact, T, K, w4=True,
+                            what=f"w4 strided {M}x{K}x{N}")
+    assert bool((yfull[:, N:] == 7.0).all())

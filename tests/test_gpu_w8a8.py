@@ -169,3 +169,21 @@ def test_lm_head_sampled_rows():
     qa, s = oracle.quant_act_per_token(xb)
     y_exact, T = oracle.gemm_w8a8_g128(qa, s, unpacked(0, "lm_head", L.K, L.N, 8), ws, rows=rows)
     assert_within_tolerance(host_bf16_bits(y)[rows], y_exact, T, L.K, what="lm_head")
+
+
+@pytest.mark.parametrize("M,K,N,kern", [(64, 1280, 392, 0), (300, 640, 520, 0), (300, 640, 520, 2), (17, 384, 40, 1)])
+def test_strided_rows(M, K, N, kern):
+    """x and y with row strides larger than K and N (ldx = K + 64, ldy = N + 24), through
+    the decode (M <= 64), prefill and 128x128 tiled kernels: the padding columns of y
+    stay untouched."""
+    xb, qw, ws = _case(5, f"st{M}-{K}-{N}", M, K, N, True)
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, oracle.gptq_unpack(qw, 8, K), ws)
+    xfull = torch.zeros((M, K + 64), dtype=torch.bfloat16, device="cuda")
+    xfull[:, :K] = dev_bf16(xb)
+    yfull = torch.full((M, N + 24), 7.0, dtype=torch.bfloat16, device="cuda")
+    i8.gemm_w8a8_g128_ex(dev(qw), dev(ws), x=xfull[:, :K], y=yfull[:, :N], kernel=kern)
+    torch.cuda.synchronize()
+    assert_within_tolerance(host_bf16_bits(yfull[:, :N].contiguous()), y_exact, T, K,
+                            what=f"strided {M}x{K}x{N} kernel {kern}")
+    assert bool((yfull[:, N:] == 7.0).all())
