@@ -273,7 +273,9 @@ W4Plan w4_plan(int M, int N, int K) {
     p.chunks = (M + kMC - 1) / kMC;
     p.tiles = (N + kTN - 1) / kTN;
     const int G = K / kGroup;
-    const int P = device_cu_count();
+    // Target 1.5 workgroups per CU: two fit on a CU (LDS), and the second one's waves
+    // hide the first one's dequantisation and barrier latencies (measured best of 1, 1.5, 2).
+    const int P = 3 * device_cu_count() / 2;
     int S = (P + p.tiles * p.chunks - 1) / (p.tiles * p.chunks);
     if (S > G) S = G;
     if (S < 1) S = 1;
