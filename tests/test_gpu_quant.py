@@ -41,6 +41,7 @@ def test_quant_act_special_rows_and_stride():
     xf[0] = 0.0                                      # all-zero row
     xf[1, :] = np.resize(np.float32([0.5, -0.5, 1.5, -2.5, 126.5, 127.0]), K)  # ties
     xf[2] = xf[3] * np.float32(2.0 ** -20)           # tiny values
+    xf[4] = xf[5] * np.float32(2.0 ** -130)          # subnormal a_scale: 1/a_scale overflows
     xb = synth.bf16_bits_from_f32(xf)
     big = np.zeros((6, K + 64), dtype=np.uint16)     # ldx > K
     big[:, :K] = xb
