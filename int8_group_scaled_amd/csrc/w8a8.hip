@@ -294,11 +294,12 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
         a_voff[j] = (int)((uint32_t)min(row, M - 1) * (uint32_t)K + (uint32_t)piece * 16u);
     }
 
-    // The 64 row scales are copied into LDS ahead of the first stage (rows past M read
-    // as 0): the first stage's wait covers this older copy too, and no register load
-    // has to be waited for before the ring starts.
+    // The 64 row scales are copied into LDS by the first copying wave ahead of its first
+    // stage (rows past M read as 0): that wave's wait for the first stage covers this older
+    // copy too (copies complete in order), so the scales are in LDS, behind the first
+    // barrier, before any chunk can end.
     float *const lds_as = reinterpret_cast<float *>(lds + RING + 256);
-    if (wave == 0) {
+    if (copier && cwave == 0) {
         const __amdgpu_buffer_rsrc_t asr =
             __builtin_amdgcn_make_buffer_rsrc((void *)a_scale, 0, (int)((uint32_t)M * 4u), kRsrcWord3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(asr, I8GS_LDS(lds_as), 4, lane * 4, 0, 0, 0);

@@ -94,6 +94,19 @@ def test_decode_workgroup_counts(wgs):
     assert_within_tolerance(host_bf16_bits(ya), y_exact, T, K, what=f"{wgs} workgroups")
 
 
+@pytest.mark.parametrize("N,wgs", [(4096, 2), (2048, 1), (1000, 1)])
+def test_decode_short_chunks(N, wgs):
+    """One group per chunk (K = 128) and tiles of several chunks: the first chunk ends right after
+    the first stage, so the row scales must already be in LDS then."""
+    M, K = 64, 128
+    xb, qw, ws = _case(7, f"chunks{N}", M, K, N, True)
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, oracle.gptq_unpack(qw, 8, K), ws)
+    y = i8.gemm_w8a8_g128_ex(dev(qw), dev(ws), x=dev_bf16(xb), kernel=i8.KERNEL_DECODE, decode_workgroups=wgs)
+    torch.cuda.synchronize()
+    assert_within_tolerance(host_bf16_bits(y), y_exact, T, K, what=f"N={N} with {wgs} workgroups")
+
+
 def test_decode_and_tiled_kernels_agree_with_oracle():
     M, K, N = 64, 2048, 384
     xb, qw, ws = _case(3, "kernels", M, K, N, True)
