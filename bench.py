@@ -238,6 +238,23 @@ def main():
     else:
         log("decode kernel sources differ from those the traffic counters were taken with: traffic = null")
 
+    # Context for the roofline: what a plain device-to-device copy reaches on this GPU
+    # (read + write bytes over time, 1 GiB each way), outside the timed region.
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * 5 * src.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
@@ -253,7 +270,9 @@ def main():
                      "traffic_unit": "bytes per launch (mean of the 4 layers; FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
                      "bytes_per_launch": "K*N + 4*N*K/128 + M*K + 4*M + 2*M*N (mean of the 4 layers: %d)"
                                          % int(g_bytes / len(layers)),
-                     "avg_launch_us": round(g_us / len(layers), 3)},
+                     "avg_launch_us": round(g_us / len(layers), 3),
+                     "measured_copy_GBps": round(copy_gbs, 1),
+                     "frac_of_measured_copy": round(achieved / copy_gbs, 4)},
         "per_layer": per_layer,
     }
 
