@@ -107,6 +107,22 @@ def test_decode_short_chunks(N, wgs):
     assert_within_tolerance(host_bf16_bits(y), y_exact, T, K, what=f"N={N} with {wgs} workgroups")
 
 
+@pytest.mark.parametrize("M,K,N,wgs", [
+    (64, 128, 48, 1), (64, 1024, 40, 1), (64, 1024, 72, 1), (64, 1024, 72, 2), (64, 1024, 136, 1),
+    (64, 1024, 136, 3), (64, 1024, 280, 1), (64, 2048, 264, 1), (20, 1024, 136, 1), (20, 1024, 136, 3),
+    (33, 1024, 72, 2),
+])
+def test_decode_partial_last_fragment(M, K, N, wgs):
+    """Chunks 48, 80 and 144 columns wide, whose last 32-column fragment reaches past the chunk:
+    whole and K-split tiles, one or two m tiles, chunks of 40, 72, 136 and 144 columns."""
+    xb, qw, ws = _case(8, f"half{M}-{K}-{N}", M, K, N, True)
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, oracle.gptq_unpack(qw, 8, K), ws)
+    y = i8.gemm_w8a8_g128_ex(dev(qw), dev(ws), x=dev_bf16(xb), kernel=i8.KERNEL_DECODE, decode_workgroups=wgs)
+    torch.cuda.synchronize()
+    assert_within_tolerance(host_bf16_bits(y), y_exact, T, K, what=f"{M}x{K}x{N} with {wgs} workgroups")
+
+
 def test_decode_and_tiled_kernels_agree_with_oracle():
     M, K, N = 64, 2048, 384
     xb, qw, ws = _case(3, "kernels", M, K, N, True)
