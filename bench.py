@@ -52,9 +52,9 @@ HBM_PEAK_GBS = 8000.0
 # DECODE_SOURCES; after any change to those files `traffic` is reported as null.
 DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h", "include/i8gs.h")
 DECODE_TRAFFIC = {
-    "sources_sha256": "fc4f72a953ac0415218d19fb923b84200ee04b7989bdc26870ad3ef3a7aba067",
-    "fetch": {"qkv": 36816801, "o_proj": 26527704, "gate_up": 192409590, "down": 107594835},
-    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456464, "down": 8528640},
+    "sources_sha256": "305535542a9bb047ba5d899053ead8d3a64e5764b9055b2d5056f26a99bd9578",
+    "fetch": {"qkv": 36816824, "o_proj": 26527628, "gate_up": 192406256, "down": 107594111},
+    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456448, "down": 8528640},
 }
 EVENT_EVERY = 8  # per-kernel HIP events on every 8th timed step (each event adds a gap)
 INT8_PEAK_TOPS = 5000.0
