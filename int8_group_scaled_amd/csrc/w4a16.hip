@@ -176,10 +176,23 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
                          a_voff, a_ins, s_half, s_voff);
         __builtin_amdgcn_sched_barrier(0);
         const char *st = lds + slot * SG::BYTES;
+        // The group's four words are dequantised first, at raised wave priority: with
+        // the two waves of a SIMD both holding VALU work, the dequantisation goes first
+        // and the MFMAs that need it start sooner (measured 2-6% faster on the decode
+        // layers at M = 8 and 64, except qkv at M = 8, 2% slower).
+        v8bf bw[4];
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) bw[ks] = dequant8x16((uint32_t)*reinterpret_cast<const int *>(st + b_off[ks]));
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
         v4f p[MT];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const v8bf b = dequant8x16((uint32_t)*reinterpret_cast<const int *>(st + b_off[ks]));
+            const v8bf b = bw[ks];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int row = mt * 16 + li;
