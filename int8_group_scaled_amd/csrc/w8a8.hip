@@ -590,8 +590,10 @@ hipError_t launch_decode(const W8A8Args &a, const DecodePlan &p, hipStream_t st)
 // activation rows (128 bytes, pieces XOR-swizzled by row % 8), the 32 packed weight
 // rows of the tile's 256 columns (rows 4..7 of every 8 shifted by 8 pieces, so the two
 // lane halves of a B read hit different banks) and their scales.  The next stage's
-// copies are issued right after the barrier that frees its slot, so they run under the
-// current stage's MFMAs.
+// copies go into the slot that the barrier at the top of the group has freed, issued
+// in four pairs (one activation and one weight copy each) after the group's first four
+// MFMA chains: issued all at once right after the barrier, they stalled every wave
+// for about a fifth of the group while the vector memory path took them in.
 //
 // Wave w owns rows 128*(w / 4) .. +127 and columns 64*(w % 4) .. +63 of the tile:
 // 4 m tiles x 2 column fragments of 32x32.  Per group it reads its B fragments (the
@@ -665,6 +667,17 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
             __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, I8GS_LDS(st + kPStageA + kPStageB + wave * 256), 4, s_voff,
                                                      (int)((uint32_t)g * (uint32_t)N * 4u), 0, 0);
     };
+    // Copy pair j of group g into stage st: activation copy j, weight copy j, and the
+    // scales with j = 0.
+    auto issue_pair = [&](char *st, int g, int j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, I8GS_LDS(st + (wave * 4 + j) * 1024), 16, a_voff[j], g * 128, 0,
+                                                 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + kPStageA + (wave * 4 + j) * 1024), 16, w_voff,
+                                                 (int)(((uint32_t)g * 32u + (uint32_t)j) * (uint32_t)N * 4u), 0, 0);
+        if (j == 0 && wave < 4)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, I8GS_LDS(st + kPStageA + kPStageB + wave * 256), 4, s_voff,
+                                                     (int)((uint32_t)g * (uint32_t)N * 4u), 0, 0);
+    };
 
     float acc[4][2][16];
 #pragma unroll
@@ -684,8 +697,11 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
         wait_vmcnt<0>();
         barrier_only();  // this stage is in; every wave is done with the other slot
         __builtin_amdgcn_sched_barrier(0);
-        if (g + 1 < G) issue(lds + ((g + 1) & 1) * kPStage, g + 1);
-        __builtin_amdgcn_sched_barrier(0);
+        // The next group's copies, into the slot this barrier freed.  The last group copies
+        // itself again into the idle slot instead of skipping them: a branch around the
+        // copies splits the compiler's schedule and spills registers.
+        char *const nst = lds + ((g + 1) & 1) * kPStage;
+        const int gn = min(g + 1, G - 1);
 
         // B fragments of this wave's two 32-column fragments, offset binary -> int8.  Lane
         // half h reads rows 8*ks + 4*h + i, whose pieces are swizzled by 8*h.
@@ -745,8 +761,10 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) a[ks] = an[ks];
             }
+            if (c < 4) issue_pair(nst, gn, c);
         }
     }
+    wait_vmcnt<0>();  // the last group's extra copies: none may still be writing LDS when the waves end
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[3][1][i] += scp * (float)pp[i];
 
