@@ -52,8 +52,8 @@ HBM_PEAK_GBS = 8000.0
 # DECODE_SOURCES; after any change to those files `traffic` is reported as null.
 DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h", "include/i8gs.h")
 DECODE_TRAFFIC = {
-    "sources_sha256": "305535542a9bb047ba5d899053ead8d3a64e5764b9055b2d5056f26a99bd9578",
-    "fetch": {"qkv": 36816824, "o_proj": 26527628, "gate_up": 192406256, "down": 107594111},
+    "sources_sha256": "d8824dd6fbe1fbd0c5df7d59826a464847d37453d12d2558ccdd972652a33b15",
+    "fetch": {"qkv": 36816912, "o_proj": 26527692, "gate_up": 192179221, "down": 107594208},
     "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456448, "down": 8528640},
 }
 EVENT_EVERY = 8  # per-kernel HIP events on every 8th timed step (each event adds a gap)
