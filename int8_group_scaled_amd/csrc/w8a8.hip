@@ -591,9 +591,9 @@ hipError_t launch_decode(const W8A8Args &a, const DecodePlan &p, hipStream_t st)
 // rows of the tile's 256 columns (rows 4..7 of every 8 shifted by 8 pieces, so the two
 // lane halves of a B read hit different banks) and their scales.  The next stage's
 // copies go into the slot that the barrier at the top of the group has freed, issued
-// in four pairs (one activation and one weight copy each) after the group's first four
-// MFMA chains: issued all at once right after the barrier, they stalled every wave
-// for about a fifth of the group while the vector memory path took them in.
+// in four pairs (one activation and one weight copy each) behind the MFMAs of the
+// group's first four chains: issued all at once right after the barrier, they stalled
+// every wave for about a fifth of the group while the vector memory path took them in.
 //
 // Wave w owns rows 128*(w / 4) .. +127 and columns 64*(w % 4) .. +63 of the tile:
 // 4 m tiles x 2 column fragments of 32x32.  Per group it reads its B fragments (the
@@ -747,6 +747,9 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
             // have VALU work the fold goes first and the next MFMA chain is reached sooner
             // (measured 2-3% faster than without).
             const int pm = c == 0 ? 3 : (c - 1) >> 1, pf = c == 0 ? 1 : (c - 1) & 1;
+            // copy pair c of the next group, issued while this chain's MFMAs run
+            __builtin_amdgcn_sched_barrier(0);
+            if (c < 4) issue_pair(nst, gn, c);
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(1);
             __builtin_amdgcn_sched_barrier(0);
@@ -761,7 +764,6 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) a[ks] = an[ks];
             }
-            if (c < 4) issue_pair(nst, gn, c);
         }
     }
     wait_vmcnt<0>();  // the last group's extra copies: none may still be writing LDS when the waves end
