@@ -52,9 +52,9 @@ HBM_PEAK_GBS = 8000.0
 # DECODE_SOURCES; after any change to those files `traffic` is reported as null.
 DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h", "include/i8gs.h")
 DECODE_TRAFFIC = {
-    "sources_sha256": "d8824dd6fbe1fbd0c5df7d59826a464847d37453d12d2558ccdd972652a33b15",
-    "fetch": {"qkv": 36816912, "o_proj": 26527692, "gate_up": 192179221, "down": 107594208},
-    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456448, "down": 8528640},
+    "sources_sha256": "f6a63a3419641725d6be3b5307433092b8ebb127ffef1ad4c89aa8b1c8fe66e4",
+    "fetch": {"qkv": 36818483, "o_proj": 26531300, "gate_up": 192388500, "down": 107598662},
+    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456496, "down": 8528640},
 }
 EVENT_EVERY = 8  # per-kernel HIP events on every 8th timed step (each event adds a gap)
 INT8_PEAK_TOPS = 5000.0
