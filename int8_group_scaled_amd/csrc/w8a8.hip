@@ -23,6 +23,7 @@
 //    through an LDS ring filled by direct buffer-to-LDS copies.
 //  * tiled (M > 64): LDS-staged 128x128 tiles, four waves of 64x64.
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -591,9 +592,13 @@ hipError_t launch_decode(const W8A8Args &a, const DecodePlan &p, hipStream_t st)
 // rows of the tile's 256 columns (rows 4..7 of every 8 shifted by 8 pieces, so the two
 // lane halves of a B read hit different banks) and their scales.  The next stage's
 // copies go into the slot that the barrier at the top of the group has freed, issued
-// in four pairs (one activation and one weight copy each) behind the MFMAs of the
-// group's first four chains: issued all at once right after the barrier, they stalled
-// every wave for about a fifth of the group while the vector memory path took them in.
+// in pairs (one activation and one weight copy each) behind the MFMAs of the group's
+// first four chains: issued all at once right after the barrier, they stalled every
+// wave for about a fifth of the group while the vector memory path took them in.
+// Waves 0-3 issue all of them, their own share and that of wave + 4 on the same SIMD:
+// the SIMD's issue arbitration favours the older wave, so waves 0-3 finished each
+// group's compute about a third sooner than waves 4-7 and then idled at the barrier;
+// taking the copies' issue stalls on themselves, they now finish closer together.
 //
 // Wave w owns rows 128*(w / 4) .. +127 and columns 64*(w % 4) .. +63 of the tile:
 // 4 m tiles x 2 column fragments of 32x32.  Per group it reads its B fragments (the
@@ -679,6 +684,17 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
                                                      (int)((uint32_t)g * (uint32_t)N * 4u), 0, 0);
     };
 
+    // Copy pair j of the share of wave + 4: its activation rows lie 128 further down
+    // (past M they lie past the end of qa: read as zeros, never stored), its weight rows
+    // 16 further down.
+    auto issue_partner = [&](char *st, int g, int j) {
+        int down = 128 * K;
+        __asm__ volatile("" : "+s"(down));  // added here, not kept in registers across the loop
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, I8GS_LDS(st + ((wave + 4) * 4 + j) * 1024), 16,
+                                                 a_voff[j] + down, g * 128, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + kPStageA + ((wave + 4) * 4 + j) * 1024), 16, w_voff,
+                                                 (int)(((uint32_t)g * 32u + (uint32_t)j + 16u) * (uint32_t)N * 4u), 0, 0);
+    };
     float acc[4][2][16];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
@@ -692,6 +708,9 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
     v16i pp = {};     // the chain folded under the next one and its scale (zero: adds an exact 0)
     float scp = 0.0f;
     issue(lds, 0);
+    // The group loop, built twice: for the copying waves 0-3 (COPIER) and for waves 4-7.
+    auto run = [&](auto copier_tag) {
+    constexpr bool COPIER = decltype(copier_tag)::value;
     for (int g = 0; g < G; ++g) {
         char *st = lds + (g & 1) * kPStage;
         wait_vmcnt<0>();
@@ -747,9 +766,14 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
             // have VALU work the fold goes first and the next MFMA chain is reached sooner
             // (measured 2-3% faster than without).
             const int pm = c == 0 ? 3 : (c - 1) >> 1, pf = c == 0 ? 1 : (c - 1) & 1;
-            // copy pair c of the next group, issued while this chain's MFMAs run
+            // copy pairs c of the next group, issued while this chain's MFMAs run
             __builtin_amdgcn_sched_barrier(0);
-            if (c < 4) issue_pair(nst, gn, c);
+            if constexpr (COPIER) {
+                if (c < 4) {
+                    issue_pair(nst, gn, c);
+                    issue_partner(nst, gn, c);
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(1);
             __builtin_amdgcn_sched_barrier(0);
@@ -766,6 +790,11 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
             }
         }
     }
+    };
+    if (wave < 4)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
     wait_vmcnt<0>();  // the last group's extra copies: none may still be writing LDS when the waves end
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[3][1][i] += scp * (float)pp[i];
