@@ -68,7 +68,6 @@ struct W4Stage {
     static constexpr int BYTES = WB + AB + SB;
     static constexpr int ACOPIES = AB / 1024;              // 1 KiB activation copies per stage
     static constexpr int AI = (ACOPIES + 7) / 8;           // per wave (extra ones repeat the last)
-    static constexpr int LPS = 1 + AI + 1;                 // copies per wave per stage
 };
 
 // The copies of one stage (group g) by this wave.
@@ -86,6 +85,23 @@ __device__ __forceinline__ void w4_issue(char *st, int g, int wave, int N, __amd
                                                  0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, I8GS_LDS(st + SG::WB + SG::AB + s_half * 256), 4, s_voff,
                                              (int)((uint32_t)g * (uint32_t)N * 4u), 0, 0);
+}
+
+// The copies of wave + 4's share, issued by wave (0-3) too: its weight rows lie 8
+// further down, its activation copies are given by a_voff / a_ins (its scales repeat
+// those of this wave and are not copied again).
+template <int MT>
+__device__ __forceinline__ void w4_issue_partner(char *st, int g, int wave, int N, __amdgpu_buffer_rsrc_t wr,
+                                                 __amdgpu_buffer_rsrc_t xr, int w_voff,
+                                                 const int (&a_voff)[W4Stage<MT>::AI],
+                                                 const int (&a_ins)[W4Stage<MT>::AI]) {
+    using SG = W4Stage<MT>;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + (wave + 4) * 1024), 16, w_voff,
+                                             (int)(((uint32_t)g * 16u + 8u) * (uint32_t)N * 4u), 0, kCpolNT);
+#pragma unroll
+    for (int j = 0; j < SG::AI; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, I8GS_LDS(st + SG::WB + a_ins[j] * 1024), 16, a_voff[j], g * 256,
+                                                 0, 0);
 }
 
 template <int MT, int D>
@@ -124,8 +140,12 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
     const __amdgpu_buffer_rsrc_t sr =
         __builtin_amdgcn_make_buffer_rsrc((void *)w_scale, 0, (int)((uint32_t)G * (uint32_t)N * 4u), kRsrcWord3);
 
-    // Copy roles (every wave issues LPS copies per stage, so one wait count serves all).
-    // Weights: wave w fills packed rows 2w, 2w+1 (32 pieces of 4 columns each).
+    // Copy roles.  The shares are per wave w: weights: packed rows 2w, 2w+1 (32 pieces of
+    // 4 columns each); activations: copies a_ins; scales: half w % 2.  Waves 0-3 issue
+    // their own share and that of wave + 4: the SIMD's issue arbitration favours the
+    // older of its two waves, and the copies' issue stalls then fall on the favoured one
+    // (1-4% faster on six of the eight decode cases, the other two unchanged).  Every
+    // copying wave issues LPSW copies per stage, so one wait count serves all.
     int w_voff;
     {
         const int r = 2 * wave + (lane >> 5), sl = lane & 31;
@@ -142,6 +162,15 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
         const int piece = sl ^ (row & 15);
         a_voff[j] = (int)(((uint32_t)min(row, mrows - 1) * (uint32_t)ldx + (uint32_t)piece * 8u) * 2u);
     }
+    int a_voffp[SG::AI], a_insp[SG::AI];  // the activation copies of wave + 4
+#pragma unroll
+    for (int j = 0; j < SG::AI; ++j) {
+        a_insp[j] = min((wave + 4) * SG::AI + j, SG::ACOPIES - 1);
+        const int row = 4 * a_insp[j] + (lane >> 4), sl = lane & 15;
+        const int piece = sl ^ (row & 15);
+        a_voffp[j] = (int)(((uint32_t)min(row, mrows - 1) * (uint32_t)ldx + (uint32_t)piece * 8u) * 2u);
+    }
+    constexpr int LPSW = 2 * (1 + SG::AI) + 1;
     // Scales: half k = wave % 2 of the tile's 128 (waves 2..7 repeat them).
     const int s_half = wave & 1;
     const int s_voff = min(n0 + 64 * s_half + lane, N - 1) * 4;
@@ -154,7 +183,10 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
 
 #pragma unroll
     for (int k = 0; k < D - 1; ++k)
-        if (k < ng) w4_issue<MT>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, sr, w_voff, a_voff, a_ins, s_half, s_voff);
+        if (k < ng && wave < 4) {
+            w4_issue<MT>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, sr, w_voff, a_voff, a_ins, s_half, s_voff);
+            w4_issue_partner<MT>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, w_voff, a_voffp, a_insp);
+        }
 
     // This lane's B words: column 16*wave + li of packed rows 4*ks + lb.
     const int cl = 16 * wave + li;
@@ -167,13 +199,15 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
     int slot = 0;
     for (int u = 0; u < ng; ++u) {
         // Copies complete in issue order and the next D-2 stages are the youngest ones.
-        if (u + D - 2 < ng) wait_vmcnt<(D - 2) * SG::LPS>();
+        if (u + D - 2 < ng) wait_vmcnt<(D - 2) * LPSW>();
         else wait_vmcnt<0>();
         barrier_only();  // this stage is in; every wave is done with the previous slot
         __builtin_amdgcn_sched_barrier(0);
-        if (u + D - 1 < ng)
-            w4_issue<MT>(lds + (slot == 0 ? D - 1 : slot - 1) * SG::BYTES, g0 + u + D - 1, wave, N, wr, xr, sr, w_voff,
-                         a_voff, a_ins, s_half, s_voff);
+        if (u + D - 1 < ng && wave < 4) {
+            char *const nst = lds + (slot == 0 ? D - 1 : slot - 1) * SG::BYTES;
+            w4_issue<MT>(nst, g0 + u + D - 1, wave, N, wr, xr, sr, w_voff, a_voff, a_ins, s_half, s_voff);
+            w4_issue_partner<MT>(nst, g0 + u + D - 1, wave, N, wr, xr, w_voff, a_voffp, a_insp);
+        }
         __builtin_amdgcn_sched_barrier(0);
         const char *st = lds + slot * SG::BYTES;
         // The group's four words are dequantised first, at raised wave priority: with
