@@ -52,9 +52,9 @@ HBM_PEAK_GBS = 8000.0
 # DECODE_SOURCES; after any change to those files `traffic` is reported as null.
 DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h", "include/i8gs.h")
 DECODE_TRAFFIC = {
-    "sources_sha256": "e1b9d9b6d739bea6392e5e1a4d03e0243d495608f70ec097dac6fef3b297f7d8",
-    "fetch": {"qkv": 36818928, "o_proj": 26534859, "gate_up": 191169868, "down": 107594528},
-    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456448, "down": 8528640},
+    "sources_sha256": "5aab6efa2d9f9902099337954a84076c011547d471d52099ac0c906197b0dbd9",
+    "fetch": {"qkv": 36820070, "o_proj": 26539230, "gate_up": 191207909, "down": 107599563},
+    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456472, "down": 8528640},
 }
 EVENT_EVERY = 8  # per-kernel HIP events on every 8th timed step (each event adds a gap)
 INT8_PEAK_TOPS = 5000.0
