@@ -692,10 +692,10 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
     // (past M they lie past the end of qa: read as zeros, never stored), its weight rows
     // 16 further down.
     auto issue_partner = [&](char *st, int g, int j) {
-        int down = 128 * K;
+        uint32_t down = 128u * (uint32_t)K;
         __asm__ volatile("" : "+s"(down));  // added here, not kept in registers across the loop
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, I8GS_LDS(st + ((wave + 4) * 4 + j) * 1024), 16,
-                                                 a_voff[j] + down, g * 128, 0, 0);
+                                                 (int)((uint32_t)a_voff[j] + down), g * 128, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + kPStageA + ((wave + 4) * 4 + j) * 1024), 16, w_voff,
                                                  (int)(((uint32_t)g * 32u + (uint32_t)j + 16u) * (uint32_t)N * 4u), 0, 0);
     };
