@@ -52,9 +52,9 @@ HBM_PEAK_GBS = 8000.0
 # DECODE_SOURCES; after any change to those files `traffic` is reported as null.
 DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h", "include/i8gs.h")
 DECODE_TRAFFIC = {
-    "sources_sha256": "5aab6efa2d9f9902099337954a84076c011547d471d52099ac0c906197b0dbd9",
-    "fetch": {"qkv": 36820070, "o_proj": 26539230, "gate_up": 191207909, "down": 107599563},
-    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456472, "down": 8528640},
+    "sources_sha256": "2736d401f8d9c34db622778ef3f5e0ab23b245d53d213f48de016b90a03c2eb6",
+    "fetch": {"qkv": 36820059, "o_proj": 26539620, "gate_up": 191797456, "down": 107599717},
+    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456448, "down": 8528640},
 }
 EVENT_EVERY = 8  # per-kernel HIP events on every 8th timed step (each event adds a gap)
 INT8_PEAK_TOPS = 5000.0
