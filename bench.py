@@ -48,11 +48,12 @@ HBM_PEAK_GBS = 8000.0
 # rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over `bench.py --traffic-probe`,
 # each counter scaled by its own reading for the probe's 256 MiB device copy
 # (FETCH_SIZE counts half the bytes read: x2.0; WRITE_SIZE: x1.0).  The figures hold
-# for the kernel sources they were taken with, identified by the SHA-256 of
-# DECODE_SOURCES; after any change to those files `traffic` is reported as null.
+# for the kernel sources they were taken with, identified by the SHA-256 of the code in
+# DECODE_SOURCES (comments and whitespace aside); after any change to that code `traffic`
+# is reported as null.
 DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h", "include/i8gs.h")
 DECODE_TRAFFIC = {
-    "sources_sha256": "2736d401f8d9c34db622778ef3f5e0ab23b245d53d213f48de016b90a03c2eb6",
+    "sources_sha256": "31a16d5980bb15c4df6f715817cbb2c38ea0fa2f6876894f3220f6106fda92fc",
     "fetch": {"qkv": 36820059, "o_proj": 26539620, "gate_up": 191797456, "down": 107599717},
     "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456448, "down": 8528640},
 }
@@ -82,11 +83,17 @@ def log(msg):
 
 
 def decode_sources_sha256():
+    """SHA-256 of the code in DECODE_SOURCES: comments removed and whitespace collapsed,
+    so that only a change to the code itself invalidates the stored counters."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in DECODE_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -688,9 +688,9 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
                                                      (int)((uint32_t)g * (uint32_t)N * 4u), 0, 0);
     };
 
-    // Copy pair j of the share of wave + 4: its activation rows lie 128 further down
-    // (past M they lie past the end of qa: read as zeros, never stored), its weight rows
-    // 16 further down.
+    // Copy pair j of the share of wave + 4: its activation rows lie 128 further down, its
+    // weight rows 16 further down.  Rows past M read zeros (past the end of qa) or, where
+    // the 32-bit offset wraps, other bytes of qa; their results are never stored.
     auto issue_partner = [&](char *st, int g, int j) {
         uint32_t down = 128u * (uint32_t)K;
         __asm__ volatile("" : "+s"(down));  // added here, not kept in registers across the loop
@@ -707,8 +707,9 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][f][i] = 0.0f;
 
-    // The fold here converts the plain int32 sums (v_cvt_f32_i32): measured a little
-    // faster in this kernel than the seeded form the decode kernel uses.
+    // The fold here converts the plain int32 sums (v_cvt_f32_i32).  The seeded form the
+    // decode kernel uses times the same but here holds its seed in 16 registers, which
+    // the A prefetch needs.
     v16i pp = {};     // the chain folded under the next one and its scale (zero: adds an exact 0)
     float scp = 0.0f;
     issue(lds, 0);
