@@ -611,6 +611,7 @@ hipError_t launch_decode(const W8A8Args &a, const DecodePlan &p, hipStream_t st)
 // the other's MFMAs.
 
 constexpr int kPB = 256;                      // prefill tile rows and columns
+constexpr int kPrefillMaxSplits = 4;          // K splits of a tile in the last round
 constexpr int kPStageA = kPB * 128;           // activation bytes of a stage
 constexpr int kPStageB = 32 * kPB * 4;        // weight bytes of a stage
 constexpr int kPStage = kPStageA + kPStageB + kPB * 4;
@@ -620,17 +621,32 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
                                                            const int32_t *__restrict__ qweight,
                                                            const float *__restrict__ w_scale,
                                                            uint16_t *__restrict__ y, int64_t ldy, int M, int N,
-                                                           int K) {
+                                                           int K, int full, int S, float *__restrict__ part,
+                                                           int *__restrict__ cnt) {
     __shared__ __attribute__((aligned(1024))) char lds[2 * kPStage];
     const int mtiles = (M + kPB - 1) / kPB, ntiles = (N + kPB - 1) / kPB;
-    // XCD-aware placement (see the decode kernel): logical tile L = nt * mtiles + mt, so
-    // the m tiles of one column tile -- which read the same weights -- share an XCD.
-    const int P = mtiles * ntiles, Q = (P + 7) >> 3;
-    const int L = (blockIdx.x & 7) * Q + (blockIdx.x >> 3);
-    if (L >= P) return;
+    const int P = mtiles * ntiles;
+    // Work items, in launch order: the first `full` tiles whole, then each of the last
+    // P - full tiles as S K-splits (they fill the last round of workgroups; a split
+    // tile's pieces are summed as in the decode kernel).  Logical tile L = nt * mtiles +
+    // mt; the whole tiles are placed XCD-aware (see the decode kernel), so the m tiles of
+    // one column tile -- which read the same weights -- share an XCD.
+    const int F8 = (full + 7) & ~7;
+    int L, s = 0;
+    if ((int)blockIdx.x < F8) {
+        L = (blockIdx.x & 7) * (F8 >> 3) + (blockIdx.x >> 3);
+        if (L >= full) return;
+    } else {
+        const int q = blockIdx.x - F8;
+        L = full + q / S;
+        s = q - (q / S) * S;
+        if (L >= P) return;
+    }
+    const bool split = L >= full;
     const int mt = L % mtiles, nt = L / mtiles;
     const int m0 = mt * kPB, n0 = nt * kPB;
     const int G = K >> 7;
+    const int g0 = split ? s * G / S : 0, g1 = split ? (s + 1) * G / S : G;  // this item's groups
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -712,20 +728,20 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
     // the A prefetch needs.
     v16i pp = {};     // the chain folded under the next one and its scale (zero: adds an exact 0)
     float scp = 0.0f;
-    issue(lds, 0);
+    issue(lds, g0);
     // The group loop, built twice: for the copying waves 0-3 (COPIER) and for waves 4-7.
     auto run = [&](auto copier_tag) {
     constexpr bool COPIER = decltype(copier_tag)::value;
-    for (int g = 0; g < G; ++g) {
-        char *st = lds + (g & 1) * kPStage;
+    for (int g = g0; g < g1; ++g) {
+        char *st = lds + ((g - g0) & 1) * kPStage;
         wait_vmcnt<0>();
         barrier_only();  // this stage is in; every wave is done with the other slot
         __builtin_amdgcn_sched_barrier(0);
         // The next group's copies, into the slot this barrier freed.  The last group copies
         // itself again into the idle slot instead of skipping them: a branch around the
         // copies splits the compiler's schedule and spills registers.
-        char *const nst = lds + ((g + 1) & 1) * kPStage;
-        const int gn = min(g + 1, G - 1);
+        char *const nst = lds + ((g + 1 - g0) & 1) * kPStage;
+        const int gn = min(g + 1, g1 - 1);
 
         // B fragments of this wave's two 32-column fragments, offset binary -> int8.  Lane
         // half h reads rows 8*ks + 4*h + i, whose pieces are swizzled by 8*h.
@@ -803,6 +819,66 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
     wait_vmcnt<0>();  // the last group's extra copies: none may still be writing LDS when the waves end
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[3][1][i] += scp * (float)pp[i];
+
+    if (split) {
+        // Publish this split's piece (fp32, lane-interleaved: value i of lane l of wave w
+        // at ((w * 128 + i) * 64 + l) floats; device-coherent), count arrivals, and let the
+        // last split to arrive sum the S pieces in split order, so the result does not
+        // depend on timing.
+        const int tt = L - full;
+        constexpr uint32_t kPiece = 8u * 128u * 64u * 4u;
+        const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)part, 0, (int)((uint32_t)(P - full) * (uint32_t)S * kPiece), kRsrcWord3);
+        const uint32_t cell0 = (uint32_t)tt * (uint32_t)S * kPiece + ((uint32_t)wave * 128u * 64u + lane) * 4u;
+#pragma unroll
+        for (int i = 0; i < 128; ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, acc[i >> 5][(i >> 4) & 1][i & 15]), pr,
+                                                  (int)cell0, (int)((uint32_t)s * kPiece + (uint32_t)i * 256u),
+                                                  kCpolSC1);
+        wait_vmcnt<0>();
+        __syncthreads();
+        int *const s_last = reinterpret_cast<int *>(lds);
+        if (threadIdx.x == 0) {
+            const int last = __hip_atomic_fetch_add(cnt + tt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+            if (last) __hip_atomic_store(cnt + tt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *s_last = last;
+        }
+        __syncthreads();
+        if (!*s_last) return;
+        // 16 values at a time: the S pieces' cells (this split's own too, already stored)
+        // all in flight, then summed in split order
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float v[kPrefillMaxSplits][16];
+#pragma unroll
+            for (int q = 0; q < kPrefillMaxSplits; ++q)
+                if (q < S) {
+#pragma unroll
+                    for (int k = 0; k < 16; ++k)
+                        v[q][k] = __builtin_bit_cast(
+                            float, __builtin_amdgcn_raw_buffer_load_b32(
+                                       pr, (int)cell0, (int)((uint32_t)q * kPiece + (uint32_t)(c * 16 + k) * 256u),
+                                       kCpolSC1));
+                }
+            // y = bf16(a_scale[row] * sum) for this chunk (m tile c / 2, fragment c % 2; the
+            // layout of the whole-tile store below)
+            const int rbase = m0 + wm * 128 + (c >> 1) * 32 + 4 * h;
+            const int cn = n0 + wn * 64 + (c & 1) * 32 + col;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                float sum = v[0][k];
+#pragma unroll
+                for (int q = 1; q < kPrefillMaxSplits; ++q)
+                    if (q < S) sum += v[q][k];
+                const int row = rbase + 8 * (k / 4) + k % 4;
+                const uint32_t off = ((uint32_t)row * (uint32_t)ldy + (uint32_t)cn) * 2u;
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(a_scale[min(row, M - 1)] * sum), yr,
+                                                      (int)(cn < N ? off : 0x80000000u), 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one chunk's loads in flight at a time
+        }
+        return;
+    }
 
     // y = bf16(a_scale[row] * acc): lane (col, h) holds column n0 + 64*wn + 32*f + col,
     // rows m0 + 128*wm + 32*mi + 8*(i/4) + 4*h + i%4.
@@ -959,8 +1035,30 @@ static bool use_decode(int M, int kernel) {
 // The decode kernel addresses y with 32-bit offsets.
 bool decode_y_fits(int64_t M, int64_t ldy) { return M * ldy * 2 < (int64_t(1) << 31); }
 
+// Prefill launch plan: whole tiles fill whole rounds of workgroups (one per CU); the
+// tiles of a last, partial round are split along K, up to kPrefillMaxSplits ways, so
+// that round is about full too.
+struct PrefillPlan {
+    int tiles, full, S;
+};
+
+PrefillPlan prefill_plan(int M, int N, int K) {
+    const int tiles = ((M + kPB - 1) / kPB) * ((N + kPB - 1) / kPB);
+    const int cus = device_cu_count(), G = K / kGroup;
+    const int tail = tiles % cus;
+    const int S = tail ? std::min(std::min(kPrefillMaxSplits, G), cus / tail) : 1;
+    if (S < 2) return {tiles, tiles, 1};
+    return {tiles, tiles - tail, S};
+}
+
+// The split tiles' fp32 pieces: 256 x 256 values per split.
+size_t prefill_workspace(const PrefillPlan &p) {
+    return p.S > 1 ? align256(size_t(p.tiles - p.full) * p.S * kPB * kPB * sizeof(float)) : 0;
+}
+
 size_t w8a8_gemm_workspace(int M, int N, int K, int kernel, int workgroups) {
     if (use_decode(M, kernel)) return decode_workspace(decode_plan(M, N, K, workgroups));
+    if (kernel != I8GS_KERNEL_TILED) return prefill_workspace(prefill_plan(M, N, K));
     return 0;
 }
 
@@ -971,9 +1069,12 @@ hipError_t launch_w8a8_gemm(const W8A8Args &a, hipStream_t s) {
         return launch_decode<2>(a, p, s);
     }
     if (a.P == nullptr && a.kernel != I8GS_KERNEL_TILED && decode_y_fits(a.M, a.ldy)) {
-        const int tiles = ((a.M + kPB - 1) / kPB) * ((a.N + kPB - 1) / kPB);
-        w8a8_prefill_kernel<<<(tiles + 7) / 8 * 8, 512, 0, s>>>(a.qa, a.a_scale, a.qweight, a.w_scale, a.y, a.ldy,
-                                                                 a.M, a.N, a.K);
+        PrefillPlan p = prefill_plan(a.M, a.N, a.K);
+        if (p.S > 1 && (a.ws == nullptr || a.ws_bytes < prefill_workspace(p) || a.counters == nullptr))
+            p = {p.tiles, p.tiles, 1};  // no room for the split pieces: whole tiles only
+        const int grid = ((p.full + 7) & ~7) + (p.tiles - p.full) * p.S;
+        w8a8_prefill_kernel<<<grid, 512, 0, s>>>(a.qa, a.a_scale, a.qweight, a.w_scale, a.y, a.ldy, a.M, a.N, a.K,
+                                                  p.full, p.S, (float *)a.ws, a.counters);
         return hipGetLastError();
     }
     dim3 grid((a.N + kTB - 1) / kTB, (a.M + kTB - 1) / kTB);
