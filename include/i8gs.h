@@ -113,8 +113,10 @@ int quant_act_per_token(const void *x, int64_t ldx, int64_t M, int64_t K, int8_t
  * split-K arrival counters at offset 0, then (W8A8) the quantised activations used
  * when x is passed (M*K bytes + 4*M, each piece rounded up to 256 bytes; always
  * counted), then the split-K partial sums (decode kernel with K split: T*S fp32
- * pieces of 64 rows by the kernel's chunk width rounded up to 32 columns).  Returns 0 when no workspace is needed
- * (W4A16 without a K split) and (size_t)-1 for invalid arguments.
+ * pieces of 64 rows by the kernel's chunk width rounded up to 32 columns; prefill
+ * kernel, M > 64: the 256 x 256 tiles of a last, partial round of workgroups, as S
+ * fp32 pieces each).  Returns 0 when no workspace is needed (W4A16 without a K
+ * split) and (size_t)-1 for invalid arguments.
  *
  * Workspace contract: the counter region must be zero when a call starts, and
  * every completed call leaves it zero again, whatever the shape.  Zero-fill a
