@@ -53,8 +53,8 @@ HBM_PEAK_GBS = 8000.0
 # is reported as null.
 DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h", "include/i8gs.h")
 DECODE_TRAFFIC = {
-    "sources_sha256": "31a16d5980bb15c4df6f715817cbb2c38ea0fa2f6876894f3220f6106fda92fc",
-    "fetch": {"qkv": 36820059, "o_proj": 26539620, "gate_up": 191797456, "down": 107599717},
+    "sources_sha256": "e6050ea0c57cb0403463c856d4ac45f424b7c2d03f40e4fdfd7da4c67a14f5bd",
+    "fetch": {"qkv": 36813840, "o_proj": 26534859, "gate_up": 190981506, "down": 107578881},
     "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456448, "down": 8528640},
 }
 EVENT_EVERY = 8  # per-kernel HIP events on every 8th timed step (each event adds a gap)
