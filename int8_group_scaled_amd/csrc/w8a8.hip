@@ -612,6 +612,8 @@ hipError_t launch_decode(const W8A8Args &a, const DecodePlan &p, hipStream_t st)
 
 constexpr int kPB = 256;                      // prefill tile rows and columns
 constexpr int kPrefillMaxSplits = 4;          // K splits of a tile in the last round
+constexpr int kPrefillMinGroups = 16;         // K groups per split, at least (the pieces'
+                                              // traffic outweighs shorter ones: o_proj)
 constexpr int kPStageA = kPB * 128;           // activation bytes of a stage
 constexpr int kPStageB = 32 * kPB * 4;        // weight bytes of a stage
 constexpr int kPStage = kPStageA + kPStageB + kPB * 4;
@@ -1036,8 +1038,8 @@ static bool use_decode(int M, int kernel) {
 bool decode_y_fits(int64_t M, int64_t ldy) { return M * ldy * 2 < (int64_t(1) << 31); }
 
 // Prefill launch plan: whole tiles fill whole rounds of workgroups (one per CU); the
-// tiles of a last, partial round are split along K, up to kPrefillMaxSplits ways, so
-// that round is about full too.
+// tiles of a last, partial round are split along K, up to kPrefillMaxSplits ways and
+// into at least kPrefillMinGroups groups each, so that round is about full too.
 struct PrefillPlan {
     int tiles, full, S;
 };
@@ -1046,7 +1048,7 @@ PrefillPlan prefill_plan(int M, int N, int K) {
     const int tiles = ((M + kPB - 1) / kPB) * ((N + kPB - 1) / kPB);
     const int cus = device_cu_count(), G = K / kGroup;
     const int tail = tiles % cus;
-    const int S = tail ? std::min(std::min(kPrefillMaxSplits, G), cus / tail) : 1;
+    const int S = tail ? std::min(std::min(kPrefillMaxSplits, G / kPrefillMinGroups), cus / tail) : 1;
     if (S < 2) return {tiles, tiles, 1};
     return {tiles, tiles - tail, S};
 }

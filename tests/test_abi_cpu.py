@@ -136,19 +136,22 @@ def test_workspace_sizes(lib):
 
 def test_prefill_split_workspace(lib):
     """Prefill (M > 64, 256 x 256 tiles, one workgroup per CU; without a GPU the CU count is
-    taken as 256): the tiles of a last, partial round are split S = min(4, K/128, 256/tail)
-    ways, each split an fp32 256 x 256 piece after the counters and quantised activations."""
+    taken as 256): the tiles of a last, partial round are split S = min(4, (K/128)/16,
+    256/tail) ways (no split below 2), each split an fp32 256 x 256 piece after the counters
+    and quantised activations."""
     import int8_group_scaled_amd as i8
     piece = 256 * 256 * 4
     base = lambda M, K: 65536 + M * K + 4 * M  # M*K and 4*M are multiples of 256 here
-    # o_proj: 16 x 20 = 320 tiles -> 256 whole + 64 split 4 ways
-    assert i8.workspace_bytes(i8.OP_W8A8, 4096, 5120, 4096) == base(4096, 4096) + 64 * 4 * piece
+    # down: 16 x 20 = 320 tiles -> 256 whole + 64 split 4 ways
+    assert i8.workspace_bytes(i8.OP_W8A8, 4096, 5120, 17408) == base(4096, 17408) + 64 * 4 * piece
+    # o_proj: the same tiles, 32 groups -> 2 ways
+    assert i8.workspace_bytes(i8.OP_W8A8, 4096, 5120, 4096) == base(4096, 4096) + 64 * 2 * piece
     # qkv: 16 x 24 = 384 tiles -> 128 split 2 ways
     assert i8.workspace_bytes(i8.OP_W8A8, 4096, 6144, 5120) == base(4096, 5120) + 128 * 2 * piece
     # exactly two rounds (16 x 32 tiles): nothing split
     assert i8.workspace_bytes(i8.OP_W8A8, 4096, 8192, 5120) == base(4096, 5120)
-    # one group (K = 128) cannot be split
-    assert i8.workspace_bytes(i8.OP_W8A8, 4096, 5120, 128) == base(4096, 128)
-    # a single tile split into 4 (of the 5 groups); the tiled kernel needs no pieces
-    assert i8.workspace_bytes(i8.OP_W8A8, 128, 256, 640) == base(128, 640) + 1 * 4 * piece
-    assert i8.workspace_bytes(i8.OP_W8A8, 128, 256, 640, i8.KERNEL_TILED) == base(128, 640)
+    # fewer than 32 groups cannot be split
+    assert i8.workspace_bytes(i8.OP_W8A8, 4096, 5120, 3968) == base(4096, 3968)
+    # two tiles split 4 ways; the tiled kernel needs no pieces
+    assert i8.workspace_bytes(i8.OP_W8A8, 128, 512, 8192) == base(128, 8192) + 2 * 4 * piece
+    assert i8.workspace_bytes(i8.OP_W8A8, 128, 512, 8192, i8.KERNEL_TILED) == base(128, 8192)

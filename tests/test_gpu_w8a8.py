@@ -134,7 +134,8 @@ def test_decode_and_tiled_kernels_agree_with_oracle():
         assert_within_tolerance(host_bf16_bits(y), y_exact, T, K, what=f"kernel {kern}")
 
 
-@pytest.mark.parametrize("M,K,N", [(600, 640, 520), (257, 256, 264), (512, 1280, 768), (300, 128, 264)])
+@pytest.mark.parametrize("M,K,N", [(600, 640, 520), (257, 256, 264), (512, 1280, 768), (300, 128, 264),
+                                   (300, 4096, 520), (130, 8192, 264)])
 def test_prefill_and_tiled_kernels_multi_tile(M, K, N):
     """M > 64: the 256x256 prefill kernel (auto) and the 128x128 tiled kernel, over
     several tiles with ragged last rows and columns, against the oracle."""
