@@ -53,9 +53,9 @@ HBM_PEAK_GBS = 8000.0
 # is reported as null.
 DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h", "include/i8gs.h")
 DECODE_TRAFFIC = {
-    "sources_sha256": "e6050ea0c57cb0403463c856d4ac45f424b7c2d03f40e4fdfd7da4c67a14f5bd",
-    "fetch": {"qkv": 36813840, "o_proj": 26534859, "gate_up": 190981506, "down": 107578881},
-    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456448, "down": 8528640},
+    "sources_sha256": "84a9eb0eea502d269f5604bcde36860788df78a2f63b532cdf897a2b3465c55b",
+    "fetch": {"qkv": 36814661, "o_proj": 26535249, "gate_up": 192737799, "down": 107581243},
+    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456544, "down": 8528640},
 }
 EVENT_EVERY = 8  # per-kernel HIP events on every 8th timed step (each event adds a gap)
 INT8_PEAK_TOPS = 5000.0
