@@ -69,6 +69,7 @@ def test_single_linear_both_modes():
 
 @pytest.mark.parametrize("M,K,N", [
     (1, 128, 8), (17, 384, 40), (63, 1024, 264), (64, 256, 520), (65, 640, 136), (100, 1152, 200), (3, 17408, 64),
+    (65, 4096, 8), (100, 8192, 200),
 ])
 def test_ragged_shapes(M, K, N):
     xb, qw, ws = _case(1, f"rag{M}-{K}-{N}", M, K, N, True)
