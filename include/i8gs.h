@@ -50,7 +50,9 @@
  *    there is no fallback path.
  *  - Shapes: K % 128 == 0 and K > 0 for the GEMMs; N % 8 == 0; M >= 0 (M == 0
  *    or N == 0 is a no-op that returns I8GS_OK).  Tensor pointers must be 16-byte
- *    aligned.  Dimensions must be below 2^31, and K*N and M*K below 2^32.
+ *    aligned.  Dimensions must be below 2^31, and K*N and M*K below 2^32.  The
+ *    W4A16 GEMM also needs (min(M, 64) - 1)*ldx*2 + K*2 < 2^31 (32-bit offsets
+ *    within a chunk of activation rows).
  *  - The device must be gfx950 (I8GS_ERR_UNSUPPORTED_DEVICE otherwise).
  */
 #ifndef I8GS_H
@@ -81,8 +83,9 @@ typedef enum {
 
 /* Kernel choice for gemm_w8a8_g128_ex(). */
 #define I8GS_KERNEL_AUTO 0   /* decode kernel for M <= 64, the 256x256-tile prefill kernel
-                                otherwise (the 128x128 tiled kernel when M*ldy*2 >= 2^31) */
-#define I8GS_KERNEL_DECODE 1 /* weight-streaming kernel (M <= 64 only) */
+                                otherwise; the 128x128 tiled kernel when R*ldy*2 >= 2^31 with
+                                R = M rounded up to 32 (M <= 64) or to 256 (M > 64) */
+#define I8GS_KERNEL_DECODE 1 /* weight-streaming kernel (M <= 64 and R*ldy*2 < 2^31 only) */
 #define I8GS_KERNEL_TILED 2  /* 128x128 LDS-tiled MFMA kernel, any M */
 
 /* ABI version of the loaded library (I8GS_ABI_VERSION at build time). */
@@ -151,8 +154,9 @@ int gemm_w8a8_g128(const void *x, int64_t ldx, const int8_t *qa, const float *a_
  * layers, K into S <= 8 parts of whole 128-wide groups (S = ceil(64 * target / N),
  * T = target / S, both clamped to the layer), so it runs T*S workgroups.  Every
  * choice computes the same exact group sums; only the fp32 fold order differs.
- * I8GS_KERNEL_DECODE is rejected when M > 64 or when M*ldy*2 >= 2^31 (32-bit
- * output offsets); I8GS_KERNEL_AUTO takes the 128x128 tiled kernel in that case.
+ * I8GS_KERNEL_DECODE is rejected when M > 64 or when R*ldy*2 >= 2^31 with R = M
+ * rounded up to 32 (32-bit output offsets); I8GS_KERNEL_AUTO takes the 128x128
+ * tiled kernel in that case.
  */
 int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float *a_scale,
                       const int32_t *qweight, const float *w_scale, void *y, int64_t ldy, int64_t M,
@@ -161,12 +165,24 @@ int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float 
 
 /*
  * The per-group int32 partials P[m, g, n] = sum_{k in group g} qa[m,k] * q[k,n]
- * of the W8A8 G128 GEMM, written to P (device int32 [M, K/128, N]) instead of
- * being folded.  Same block code as gemm_w8a8_g128; used to check the integer
- * stage bit-exactly.
+ * of the W8A8 G128 GEMM (Qwen3.8-27B W8A8 card, "Quantization details": int8 x
+ * int8 products summed per 128-wide K block), written to P (device int32
+ * [M, K/128, N]) instead of being folded.  The call runs the kernel and the launch
+ * plan that gemm_w8a8_g128 runs for the same M (the decode kernel for M <= 64 with
+ * its column tiles and K splits, the 256 x 256 prefill kernel above, including
+ * its K-split last round), in a mode that stores each MFMA chain's group sum --
+ * for the decode kernel decoded from its seeded accumulator exactly as its fold
+ * decodes it -- where that kernel would fold it.  It checks the integer stage
+ * bit-exactly.  Needs no workspace.  Results are bit-exact.
  */
 int gemm_w8a8_g128_group_partials(const int8_t *qa, const int32_t *qweight, int32_t *P,
                                   int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Same, with the kernel (I8GS_KERNEL_*) and decode workgroup target chosen as for
+ * gemm_w8a8_g128_ex(); I8GS_KERNEL_TILED runs the 128 x 128 tiled kernel.  Every
+ * choice writes the same P. */
+int gemm_w8a8_g128_group_partials_ex(const int8_t *qa, const int32_t *qweight, int32_t *P, int64_t M,
+                                     int64_t N, int64_t K, int kernel, int decode_workgroups, void *stream);
 
 /*
  * W4A16 g128 weight-only linear (Qwen3.8-27B-DFlash2 W4A16 card, property and

@@ -37,7 +37,8 @@ KERNEL_TILED = 2
 EXPORTS = (
     "i8gs_abi_version", "i8gs_last_error", "i8gs_status_string", "quant_act_per_token",
     "i8gs_workspace_bytes", "i8gs_workspace_bytes_ex", "gemm_w8a8_g128", "gemm_w8a8_g128_ex",
-    "gemm_w8a8_g128_group_partials", "gemm_w4a16_g128", "gptq_unpack", "gptq_quantize_rtn",
+    "gemm_w8a8_g128_group_partials", "gemm_w8a8_g128_group_partials_ex", "gemm_w4a16_g128", "gptq_unpack",
+    "gptq_quantize_rtn",
 )
 
 _lib = None
@@ -77,11 +78,12 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_w8a8_g128.argtypes = [P, I64, P, P, P, P, P, I64, I64, I64, I64, P, S, P]
     lib.gemm_w8a8_g128_ex.argtypes = [P, I64, P, P, P, P, P, I64, I64, I64, I64, I, I, P, S, P]
     lib.gemm_w8a8_g128_group_partials.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.gemm_w8a8_g128_group_partials_ex.argtypes = [P, P, P, I64, I64, I64, I, I, P]
     lib.gemm_w4a16_g128.argtypes = [P, I64, P, P, P, I64, I64, I64, I64, P, S, P]
     lib.gptq_unpack.argtypes = [P, P, I, I64, I64, P, P, P]
     lib.gptq_quantize_rtn.argtypes = [P, I, I64, I64, P, P, P]
     for name in ("quant_act_per_token", "gemm_w8a8_g128", "gemm_w8a8_g128_ex", "gemm_w8a8_g128_group_partials",
-                 "gemm_w4a16_g128", "gptq_unpack", "gptq_quantize_rtn"):
+                 "gemm_w8a8_g128_group_partials_ex", "gemm_w4a16_g128", "gptq_unpack", "gptq_quantize_rtn"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -216,8 +218,10 @@ def gemm_w8a8_g128(qweight, w_scale, x=None, qa=None, a_scale=None, y=None) -> t
     return gemm_w8a8_g128_ex(qweight, w_scale, x=x, qa=qa, a_scale=a_scale, y=y)
 
 
-def gemm_w8a8_g128_group_partials(qa: torch.Tensor, qweight: torch.Tensor) -> torch.Tensor:
-    """int32 P [M, K/128, N] of per-group integer dot products."""
+def gemm_w8a8_g128_group_partials(qa: torch.Tensor, qweight: torch.Tensor, kernel: int = KERNEL_AUTO,
+                                  decode_workgroups: int = 0) -> torch.Tensor:
+    """int32 P [M, K/128, N] of per-group integer dot products, from the kernel and plan
+    gemm_w8a8_g128_ex would use with the same kernel / workgroup choice."""
     _need(qa, "qa", torch.int8, 2)
     _need(qweight, "qweight", torch.int32, 2)
     if not qa.is_contiguous() or not qweight.is_contiguous():
@@ -227,8 +231,8 @@ def gemm_w8a8_g128_group_partials(qa: torch.Tensor, qweight: torch.Tensor) -> to
     if qweight.shape[0] * 4 != K:
         raise ValueError("qweight rows must be K/4")
     P = torch.empty((M, K // 128, N), dtype=torch.int32, device=qa.device)
-    _raise(load_library().gemm_w8a8_g128_group_partials(_ptr(qa), _ptr(qweight), _ptr(P), M, N, K,
-                                                        _stream(qa.device)))
+    _raise(load_library().gemm_w8a8_g128_group_partials_ex(_ptr(qa), _ptr(qweight), _ptr(P), M, N, K, kernel,
+                                                           decode_workgroups, _stream(qa.device)))
     return P
 
 

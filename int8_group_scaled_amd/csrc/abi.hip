@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -195,7 +196,8 @@ int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float 
     I8GS_TRY(check_ld(ldy, N, "ldy"));
     if (kernel == I8GS_KERNEL_DECODE && !decode_y_fits(M, ldy))
         return fail(I8GS_ERR_UNSUPPORTED_SHAPE,
-                    fmt("the decode kernel needs M*ldy*2 < 2^31 bytes of y (M=%lld ldy=%lld)", M, ldy));
+                    fmt("the decode kernel needs R*ldy*2 < 2^31 bytes of y, R = M rounded up to 32 (M=%lld ldy=%lld)",
+                        M, ldy));
     const size_t gemm_ws = w8a8_gemm_workspace((int)M, (int)N, (int)K, kernel, decode_workgroups);
     const size_t qbytes = w8a8_quant_bytes(M, K);
     const size_t need = kCounterBytes + qbytes + gemm_ws;
@@ -230,18 +232,31 @@ int gemm_w8a8_g128(const void *x, int64_t ldx, const int8_t *qa, const float *a_
                              workspace, workspace_bytes, stream);
 }
 
-int gemm_w8a8_g128_group_partials(const int8_t *qa, const int32_t *qweight, int32_t *P,
-                                  int64_t M, int64_t N, int64_t K, void *stream) {
+int gemm_w8a8_g128_group_partials_ex(const int8_t *qa, const int32_t *qweight, int32_t *P, int64_t M,
+                                     int64_t N, int64_t K, int kernel, int decode_workgroups, void *stream) {
     I8GS_TRY(check_dims(M, N, K, true));
+    if (kernel < I8GS_KERNEL_AUTO || kernel > I8GS_KERNEL_TILED)
+        return fail(I8GS_ERR_INVALID_ARG, fmt("kernel=%lld is not one of I8GS_KERNEL_*", kernel));
+    if (decode_workgroups < 0)
+        return fail(I8GS_ERR_INVALID_ARG, fmt("decode_workgroups=%lld must be >= 0", decode_workgroups));
+    if (kernel == I8GS_KERNEL_DECODE && M > 64)
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("the decode kernel takes M <= 64 (M=%lld)", M));
     if (M == 0 || N == 0) return ok();
     I8GS_TRY(check_ptr(qa, "qa"));
     I8GS_TRY(check_ptr(qweight, "qweight"));
     I8GS_TRY(check_ptr(P, "P"));
     I8GS_TRY(check_device());
-    W8A8Args a{qa, nullptr, qweight, nullptr, nullptr, 0, P, (int)M, (int)N, (int)K, I8GS_KERNEL_TILED, 0,
-               nullptr, nullptr, 0};
+    // The scale pointers are not read in this mode (their copies have an empty range); they
+    // point at valid memory all the same.
+    W8A8Args a{qa, (const float *)qa, qweight, (const float *)qweight, nullptr, 0, P, (int)M, (int)N, (int)K, kernel,
+               decode_workgroups, nullptr, nullptr, 0};
     I8GS_TRY(hip_check(launch_w8a8_gemm(a, (hipStream_t)stream), "group partials launch"));
     return ok();
+}
+
+int gemm_w8a8_g128_group_partials(const int8_t *qa, const int32_t *qweight, int32_t *P,
+                                  int64_t M, int64_t N, int64_t K, void *stream) {
+    return gemm_w8a8_g128_group_partials_ex(qa, qweight, P, M, N, K, I8GS_KERNEL_AUTO, 0, stream);
 }
 
 int gemm_w4a16_g128(const void *x, int64_t ldx, const int32_t *qweight, const float *w_scale,
@@ -255,6 +270,11 @@ int gemm_w4a16_g128(const void *x, int64_t ldx, const int32_t *qweight, const fl
     I8GS_TRY(check_ptr(w_scale, "w_scale"));
     I8GS_TRY(check_ptr(y, "y"));
     I8GS_TRY(check_ld(ldy, N, "ldy"));
+    // the kernel addresses a chunk of up to 64 activation rows with 32-bit byte offsets
+    if (((std::min<int64_t>(M, 64) - 1) * ldx + K) * 2 >= (int64_t(1) << 31))
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE,
+                    fmt("the W4A16 kernel needs (min(M,64)-1)*ldx*2 + K*2 < 2^31 bytes of x (M=%lld ldx=%lld)", M,
+                        ldx));
     const size_t part = w4a16_gemm_workspace((int)M, (int)N, (int)K);
     const size_t need = part ? kCounterBytes + part : 0;
     if (need > 0) {

@@ -50,9 +50,11 @@ struct W8A8Args {
     size_t ws_bytes;
 };
 size_t w8a8_gemm_workspace(int M, int N, int K, int kernel, int workgroups);
-// Whether y (M rows of stride ldy) is small enough for the decode kernel's 32-bit
-// offsets; an automatic choice falls back to the tiled kernel when it is not.
+// Whether y (M rows of stride ldy, padded to the kernel's row tiles) is small enough for
+// the decode / prefill kernel's 32-bit offsets; an automatic choice falls back to the
+// tiled kernel when it is not.
 bool decode_y_fits(int64_t M, int64_t ldy);
+bool prefill_y_fits(int64_t M, int64_t ldy);
 hipError_t launch_w8a8_gemm(const W8A8Args &a, hipStream_t s);
 
 struct W4A16Args {

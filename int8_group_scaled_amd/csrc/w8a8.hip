@@ -4,24 +4,25 @@
 // int8 x int8 compute at every decode and prefill shape with one weight scale per
 // 128-wide K block.  Flint INT8 card, format table: GPTQ qweight/scales, symmetric,
 // group 128, no g_idx.  For each 128-wide group the int8 products are summed exactly
-// in an int32 MFMA accumulator (v_mfma_i32_16x16x64_i8, two per group), converted to
-// fp32 and folded with that group's per-column scale; the row scale and the bf16
-// rounding are applied once at the end.
-//
-// MFMA operand layout used here (16x16x64 i8): lane l holds row (l % 16) of A and
-// column (l % 16) of B, 16 consecutive K bytes starting at 16 * (l / 16) within a
-// 64-wide K step.  A and B use the same K placement, so the product is the plain
-// dot product whatever order the hardware walks K in.  The 16x16 int32 result puts
-// column (l % 16), rows 4 * (l / 16) + r (r = 0..3) in lane l.
+// in an int32 MFMA accumulator, converted to fp32 and folded with that group's
+// per-column scale; the row scale and the bf16 rounding are applied once at the end.
 //
 // GPTQ codes are offset binary (q + 128); XOR 0x80 per byte turns a code into the
 // two's-complement int8 value of q.
 //
-// Two kernels:
-//  * decode (M <= 64): bound by streaming the weights from HBM.  About one
-//    workgroup per CU streams its columns (and, for narrow layers, a part of K)
-//    through an LDS ring filled by direct buffer-to-LDS copies.
-//  * tiled (M > 64): LDS-staged 128x128 tiles, four waves of 64x64.
+// Three kernels:
+//  * decode (M <= 64, w8a8_decode_kernel): bound by streaming the weights from HBM.
+//    About one workgroup per CU streams its columns (and, for narrow layers, a part
+//    of K) through an LDS ring filled by direct buffer-to-LDS copies;
+//    v_mfma_i32_32x32x32_i8, four per 32x32 block and group.
+//  * prefill (M > 64, w8a8_prefill_kernel): 256 x 256 output tiles, eight waves of
+//    128 x 64; v_mfma_i32_32x32x32_i8 as in the decode kernel.
+//  * tiled (w8a8_tiled_kernel): 128 x 128 tiles, four waves of 64 x 64,
+//    v_mfma_i32_16x16x64_i8; the fallback when y is too large for 32-bit offsets
+//    (or when asked for by I8GS_KERNEL_TILED).
+// Each kernel also has a partials mode that writes the exact int32 group sums
+// P[m, g, n] instead of folding them: the same loads, LDS layout and MFMA chains,
+// with the fold and the output stage replaced by a store of each chain's result.
 #include <algorithm>
 #include <type_traits>
 
@@ -76,10 +77,6 @@ __device__ __forceinline__ v4i flip(v4i v) {
 
 constexpr int kMaxSplits = 8;
 
-#ifndef I8GS_DECODE_SPLIT_CHAIN
-#define I8GS_DECODE_SPLIT_CHAIN 0  // 1: each fragment's group sum as two MFMA chains of two K steps
-#endif
-
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ v16i mfma32_i8(v4i a, v4i b, v16i c) {
@@ -90,8 +87,9 @@ __device__ __forceinline__ v16i mfma32_i8(v4i a, v4i b, v16i c) {
 // from the accumulator value kSumSeed (the fp32 bit pattern of 1/(2*pi), an inline
 // constant of the MFMA's C operand) instead of 0.  Read as an fp32 number, the int32
 // result kSumSeed + S equals f_seed + S * 2^-26 exactly while it stays in the seed's
-// binade [1/8, 1/4), i.e. for -2291075 <= S <= 6097532, and a sum of 128 products of
-// two int8 values lies within +-2097152.  f_seed minus that number is then exact
+// binade [1/8, 1/4) (bit patterns 0x3E000000 .. 0x3E7FFFFF), i.e. for
+// -2292099 <= S <= 6096508, and a sum of 128 products of two int8 values lies within
+// +-2097152.  f_seed minus that number is then exact
 // (Sterbenz): -S * 2^-26 for one full-rate VALU op with an inline constant, where an
 // int-to-float convert costs a half-rate one, and multiplying it by -scale * 2^26
 // gives exactly the product scale * S that the fold adds.  (Scales must keep
@@ -111,9 +109,12 @@ __device__ __forceinline__ float seeded_sum(int r) {
     return __builtin_bit_cast(float, kSumSeed) - __builtin_bit_cast(float, r);
 }
 
-template <int M2, int TN, int W>
+// PARTIALS is part of the shape so that each kernel instantiation has shape types of
+// its own: a device function template taking buffer resources, used with the same
+// shape from two kernel instantiations, fails overload resolution in hipcc's host pass.
+template <int M2, int TN, int W, bool PARTIALS>
 struct DecodeShape {
-    static_assert((M2 == 1 || M2 == 2) && (W == 4 || W == 8) && TN % 8 == 0 && TN >= 8 && TN <= 256,
+    static_assert((M2 == 1 || M2 == 2) && W == 8 && TN % 8 == 0 && TN >= 8 && TN <= 256,
                   "unsupported decode shape");
     static constexpr int NF = (TN + 31) / 32;          // 32-column fragments of a chunk
     static constexpr int WPM = W / M2;                 // waves per m tile
@@ -184,23 +185,6 @@ __device__ __forceinline__ void decode_mfma(const char *st, int wave, int lane, 
             for (int i = 0; i < 4; ++i) b[j][ks][i] = wcol[(8 * ks + 4 * h + i) * (S::PPR * 4)];
         sc[j] = reinterpret_cast<const float *>(st + S::WB + S::AB)[c] * kSumScale;
     }
-#if I8GS_DECODE_SPLIT_CHAIN
-    // two independent chains of two K steps each, joined by an exact int32 add
-    v16i q[S::NFW];
-#pragma unroll
-    for (int ks = 0; ks < 4; ks += 2)
-#pragma unroll
-        for (int j = 0; j < S::NFW; ++j) {
-            if (j == S::NFW - 1 && !last_live) break;
-            p[j] = mfma32_i8(a[ks], b[j][ks] ^ (int)0x80808080, ks == 0 ? sum_seed() : p[j]);
-            q[j] = mfma32_i8(a[ks + 1], b[j][ks + 1] ^ (int)0x80808080, ks == 0 ? v16i{} : q[j]);
-        }
-#pragma unroll
-    for (int j = 0; j < S::NFW; ++j) {
-        if (j == S::NFW - 1 && !last_live) break;
-        p[j] += q[j];
-    }
-#else
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -208,7 +192,6 @@ __device__ __forceinline__ void decode_mfma(const char *st, int wave, int lane, 
             if (j == S::NFW - 1 && !last_live) break;
             p[j] = mfma32_i8(a[ks], b[j][ks] ^ (int)0x80808080, ks == 0 ? sum_seed() : p[j]);
         }
-#endif
 }
 
 // The fold of one stage: acc += scale * group sum (sc holds scale * -2^26, p the seeded
@@ -224,7 +207,28 @@ __device__ __forceinline__ void decode_fold(float (&acc)[S::NFW][16], const v16i
     }
 }
 
-template <int M2, int TN, int W, int D>
+// Partials mode: the exact int32 group sums of one stage, decoded from the seeded
+// MFMA results exactly as the fold decodes them (seeded_sum times -2^26 is the sum
+// itself), written to P[row, g, column] for the rows below M and the chunk's columns.
+template <class S>
+__device__ __forceinline__ void decode_store_partials(int32_t *__restrict__ P, const v16i (&p)[S::NFW], int wave,
+                                                      int lane, bool last_live, int row0, int kb, int kw, int g,
+                                                      int M, int N, int G) {
+    const int col = lane & 31;
+#pragma unroll
+    for (int j = 0; j < S::NFW; ++j) {
+        if (j == S::NFW - 1 && !last_live) break;
+        const int cl = S::frag(wave, j) * 32 + col;
+        if (cl >= kw) continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = row0 + 8 * (i / 4) + i % 4;
+            if (row < M) P[((int64_t)row * G + g) * N + kb + cl] = (int)(seeded_sum(p[j][i]) * kSumScale);
+        }
+    }
+}
+
+template <int M2, int TN, int W, int D, bool PARTIALS>
 __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__restrict__ qa,
                                                           const float *__restrict__ a_scale,
                                                           const int32_t *__restrict__ qweight,
@@ -232,7 +236,9 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
                                                           uint16_t *__restrict__ y, int64_t ldy, int M, int N, int K,
                                                           int T, int S, float *__restrict__ part,
                                                           int *__restrict__ cnt) {
-    using SH = DecodeShape<M2, TN, W>;
+    using SH = DecodeShape<M2, TN, W, PARTIALS>;
+    // partials mode: `part` is the int32 output P [M, K/128, N] (there is no split reduction)
+    int32_t *const Pout = reinterpret_cast<int32_t *>(part);
     constexpr int NFW = SH::NFW;
     // At least 82 KiB, so that no CU takes two of these workgroups while another has
     // none (the grid is about one workgroup per CU).
@@ -267,16 +273,18 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
     const int col = lane & 31, h = lane >> 5;
     const int row0 = SH::mtile(wave) * 32 + 4 * h;  // this lane's output rows: row0 + 8*(i/4) + i%4
 
-    // byte offsets fit 32 bits: K*N < 2^32, M*K < 2^32 and M*ldy*2 < 2^31 are checked
+    // byte offsets fit 32 bits: K*N < 2^32, M*K < 2^32 and 32*M2*ldy*2 < 2^31 are checked
     // before launch
     const __amdgpu_buffer_rsrc_t wr =
         __builtin_amdgcn_make_buffer_rsrc((void *)qweight, 0, (int)((uint32_t)K * (uint32_t)N), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t ar =
         __builtin_amdgcn_make_buffer_rsrc((void *)qa, 0, (int)((uint32_t)M * (uint32_t)K), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t sr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)w_scale, 0, (int)((uint32_t)G * (uint32_t)N * 4u), kRsrcWord3);
-    // y stores go through a descriptor whose range check drops rows >= M (columns
-    // past the chunk are sent past the end explicitly).
+    // (partials mode: no scales are read; an empty range turns those copies into zeros)
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)w_scale, 0, PARTIALS ? 0 : (int)((uint32_t)G * (uint32_t)N * 4u), kRsrcWord3);
+    // y stores go through a descriptor whose range check drops rows >= M: their offsets
+    // are at least M*ldy*2 and below 2^31 (the padded rows, 32*M2 of them, are checked
+    // before launch); columns past the chunk are sent past the end explicitly.
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)y, 0, (int)(((uint32_t)(M - 1) * (uint32_t)ldy + (uint32_t)N) * 2u), kRsrcWord3);
 
@@ -290,7 +298,7 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
     // extra fragments (frag(w, j) = w / M2 + j * 8 / M2), or, with 64-column chunks,
     // waves 4-7 have no fragment at all.
     const int cwave = wave & 3;
-    const bool copier = W == 4 || (SH::NF == SH::WPM ? wave < 4 : wave >= 4);
+    const bool copier = SH::NF == SH::WPM ? wave < 4 : wave >= 4;
     int a_voff[SH::AI];
 #pragma unroll
     for (int j = 0; j < SH::AI; ++j) {
@@ -306,7 +314,7 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
     float *const lds_as = reinterpret_cast<float *>(lds + RING + 256);
     if (copier && cwave == 0) {
         const __amdgpu_buffer_rsrc_t asr =
-            __builtin_amdgcn_make_buffer_rsrc((void *)a_scale, 0, (int)((uint32_t)M * 4u), kRsrcWord3);
+            __builtin_amdgcn_make_buffer_rsrc((void *)a_scale, 0, PARTIALS ? 0 : (int)((uint32_t)M * 4u), kRsrcWord3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(asr, I8GS_LDS(lds_as), 4, lane * 4, 0, 0, 0);
     }
 
@@ -370,7 +378,18 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
         v16i p_cur[NFW];
         float sc_cur[NFW];
         decode_mfma<SH>(lds + slot * SH::STAGE, wave, lane, last_live, p_cur, sc_cur);
-        decode_fold<SH>(acc, p_prev, sc_prev, last_live);
+        if constexpr (PARTIALS) {
+            const int pb = c0 + 8 * (kc * wg8 / nch), pw = c0 + 8 * ((kc + 1) * wg8 / nch) - pb;
+            decode_store_partials<SH>(Pout, p_cur, wave, lane, last_live, row0, pb, pw, g0 + kk, M, N, G);
+            slot = slot == D - 1 ? 0 : slot + 1;
+            if (++kk == ng) {
+                kk = 0;
+                ++kc;
+            }
+            continue;
+        } else {
+            decode_fold<SH>(acc, p_prev, sc_prev, last_live);
+        }
 #pragma unroll
         for (int j = 0; j < NFW; ++j) {
             p_prev[j] = p_cur[j];
@@ -409,7 +428,7 @@ __global__ __launch_bounds__(W * 64) void w8a8_decode_kernel(const int8_t *__res
             }
         }
     }
-    if (S == 1) return;
+    if (S == 1 || PARTIALS) return;
 
     // ---- split tile (one chunk): publish this split's piece (fp32 [row][32*NF]; every
     // fragment lane, also those past the chunk, has its own place; device-coherent),
@@ -555,33 +574,30 @@ size_t decode_workspace(const DecodePlan &p) {
     return p.S > 1 ? align256(size_t(p.T) * p.S * 64 * ((p.tn + 31) / 32 * 32) * sizeof(float)) : 0;
 }
 
-#ifndef I8GS_DECODE_WAVES
-#define I8GS_DECODE_WAVES 8  // two per SIMD, so one wave's latencies hide behind the other's work
-#endif
-
-template <int M2, int TN>
+template <int M2, int TN, bool PARTIALS>
 hipError_t launch_decode_tn(const W8A8Args &a, const DecodePlan &p, hipStream_t st) {
-    constexpr int W = I8GS_DECODE_WAVES;
+    constexpr int W = 8;  // two per SIMD, so one wave's latencies hide behind the other's work
     // as many stages as fit in LDS, up to I8GS_DECODE_STAGES
-    constexpr int FIT = (160 * 1024 - 16) / DecodeShape<M2, TN, W>::STAGE;
+    constexpr int FIT = (160 * 1024 - 16) / DecodeShape<M2, TN, W, PARTIALS>::STAGE;
     constexpr int D = FIT < I8GS_DECODE_STAGES ? FIT : I8GS_DECODE_STAGES;
-    w8a8_decode_kernel<M2, TN, W, D><<<(p.T * p.S + 7) / 8 * 8, W * 64, 0, st>>>(
-        a.qa, a.a_scale, a.qweight, a.w_scale, a.y, a.ldy, a.M, a.N, a.K, p.T, p.S, (float *)a.ws, a.counters);
+    w8a8_decode_kernel<M2, TN, W, D, PARTIALS><<<(p.T * p.S + 7) / 8 * 8, W * 64, 0, st>>>(
+        a.qa, a.a_scale, a.qweight, a.w_scale, a.y, a.ldy, a.M, a.N, a.K, p.T, p.S,
+        PARTIALS ? reinterpret_cast<float *>(a.P) : (float *)a.ws, a.counters);
     return hipGetLastError();
 }
 
-template <int M2>
+template <int M2, bool PARTIALS>
 hipError_t launch_decode(const W8A8Args &a, const DecodePlan &p, hipStream_t st) {
     switch (p.tn) {
-        case 32: return launch_decode_tn<M2, 32>(a, p, st);
-        case 48: return launch_decode_tn<M2, 48>(a, p, st);
-        case 64: return launch_decode_tn<M2, 64>(a, p, st);
-        case 80: return launch_decode_tn<M2, 80>(a, p, st);
-        case 96: return launch_decode_tn<M2, 96>(a, p, st);
-        case 128: return launch_decode_tn<M2, 128>(a, p, st);
-        case 144: return launch_decode_tn<M2, 144>(a, p, st);
-        case 192: return launch_decode_tn<M2, 192>(a, p, st);
-        default: return launch_decode_tn<M2, 256>(a, p, st);
+        case 32: return launch_decode_tn<M2, 32, PARTIALS>(a, p, st);
+        case 48: return launch_decode_tn<M2, 48, PARTIALS>(a, p, st);
+        case 64: return launch_decode_tn<M2, 64, PARTIALS>(a, p, st);
+        case 80: return launch_decode_tn<M2, 80, PARTIALS>(a, p, st);
+        case 96: return launch_decode_tn<M2, 96, PARTIALS>(a, p, st);
+        case 128: return launch_decode_tn<M2, 128, PARTIALS>(a, p, st);
+        case 144: return launch_decode_tn<M2, 144, PARTIALS>(a, p, st);
+        case 192: return launch_decode_tn<M2, 192, PARTIALS>(a, p, st);
+        default: return launch_decode_tn<M2, 256, PARTIALS>(a, p, st);
     }
 }
 
@@ -618,13 +634,15 @@ constexpr int kPStageA = kPB * 128;           // activation bytes of a stage
 constexpr int kPStageB = 32 * kPB * 4;        // weight bytes of a stage
 constexpr int kPStage = kPStageA + kPStageB + kPB * 4;
 
-__global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restrict__ qa,
-                                                           const float *__restrict__ a_scale,
-                                                           const int32_t *__restrict__ qweight,
-                                                           const float *__restrict__ w_scale,
-                                                           uint16_t *__restrict__ y, int64_t ldy, int M, int N,
-                                                           int K, int full, int S, float *__restrict__ part,
-                                                           int *__restrict__ cnt) {
+// The kernel body, built twice: folding into y (PARTIALS false) and writing the exact
+// group sums to Pout (PARTIALS true), each called by a plain kernel: lambdas that call
+// AMDGPU builtins inside a kernel template lose the host-side launch stub.
+template <bool PARTIALS>
+__device__ __forceinline__ void prefill_body(const int8_t *__restrict__ qa, const float *__restrict__ a_scale,
+                                             const int32_t *__restrict__ qweight, const float *__restrict__ w_scale,
+                                             uint16_t *__restrict__ y, int64_t ldy, int M, int N, int K, int full,
+                                             int S, float *__restrict__ part, int *__restrict__ cnt,
+                                             int32_t *__restrict__ Pout) {
     __shared__ __attribute__((aligned(1024))) char lds[2 * kPStage];
     const int mtiles = (M + kPB - 1) / kPB, ntiles = (N + kPB - 1) / kPB;
     const int P = mtiles * ntiles;
@@ -659,8 +677,9 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
         __builtin_amdgcn_make_buffer_rsrc((void *)qweight, 0, (int)((uint32_t)K * (uint32_t)N), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t ar =
         __builtin_amdgcn_make_buffer_rsrc((void *)qa, 0, (int)((uint32_t)M * (uint32_t)K), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t sr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)w_scale, 0, (int)((uint32_t)G * (uint32_t)N * 4u), kRsrcWord3);
+    // (partials mode: no scales are read; an empty range turns those copies into zeros)
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)w_scale, 0, PARTIALS ? 0 : (int)((uint32_t)G * (uint32_t)N * 4u), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)y, 0, (int)(((uint32_t)(M - 1) * (uint32_t)ldy + (uint32_t)N) * 2u), kRsrcWord3);
 
@@ -797,16 +816,30 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
                     issue_partner(nst, gn, c);
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_setprio(1);
-            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (PARTIALS) {
+                // this chain's exact group sums: rows m0 + 128*wm + 32*mi + 8*(i/4) + 4*h + i%4,
+                // column n0 + 64*wn + 32*f + col
+                const int rbase = m0 + wm * 128 + mi * 32 + 4 * h;
+                const int cn = n0 + wn * 64 + f * 32 + col;
+                if (cn < N) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[pm][pf][i] += scp * (float)pp[i];
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_setprio(0);
-            __builtin_amdgcn_sched_barrier(0);
-            pp = p;
-            scp = sc[f];
+                    for (int i = 0; i < 16; ++i) {
+                        const int row = rbase + 8 * (i / 4) + i % 4;
+                        if (row < M) Pout[((int64_t)row * G + g) * N + cn] = p[i];
+                    }
+                }
+            } else {
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[pm][pf][i] += scp * (float)pp[i];
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_sched_barrier(0);
+                pp = p;
+                scp = sc[f];
+            }
             if (f == 1) {
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) a[ks] = an[ks];
@@ -819,6 +852,7 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
     else
         run(std::false_type{});
     wait_vmcnt<0>();  // the last group's extra copies: none may still be writing LDS when the waves end
+    if constexpr (PARTIALS) return;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[3][1][i] += scp * (float)pp[i];
 
@@ -902,6 +936,25 @@ __global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restr
             }
         }
     }
+}
+
+__global__ __launch_bounds__(512) void w8a8_prefill_kernel(const int8_t *__restrict__ qa,
+                                                           const float *__restrict__ a_scale,
+                                                           const int32_t *__restrict__ qweight,
+                                                           const float *__restrict__ w_scale,
+                                                           uint16_t *__restrict__ y, int64_t ldy, int M, int N,
+                                                           int K, int full, int S, float *__restrict__ part,
+                                                           int *__restrict__ cnt) {
+    prefill_body<false>(qa, a_scale, qweight, w_scale, y, ldy, M, N, K, full, S, part, cnt, nullptr);
+}
+
+__global__ __launch_bounds__(512) void w8a8_prefill_partials_kernel(const int8_t *__restrict__ qa,
+                                                                    const int32_t *__restrict__ qweight, int M,
+                                                                    int N, int K, int full, int S,
+                                                                    int32_t *__restrict__ P) {
+    // the scale pointers are not read (empty copy range); they point at valid memory
+    prefill_body<true>(qa, (const float *)qa, qweight, (const float *)qweight, nullptr, 0, M, N, K, full, S, nullptr,
+                       nullptr, P);
 }
 
 // ------------------------------------------------------------------ tiled kernel (group partials; M > 64 fallback)
@@ -1034,8 +1087,12 @@ static bool use_decode(int M, int kernel) {
     return M <= 64;
 }
 
-// The decode kernel addresses y with 32-bit offsets.
-bool decode_y_fits(int64_t M, int64_t ldy) { return M * ldy * 2 < (int64_t(1) << 31); }
+// The decode and prefill kernels address y with 32-bit offsets and drop the rows past M
+// by the y descriptor's range check, so the offsets of all the rows a launch covers --
+// M rounded up to the 32-row m tiles (decode) or to the 256-row tiles (prefill) --
+// must stay below 2^31 (no wrap back into range).
+bool decode_y_fits(int64_t M, int64_t ldy) { return (M <= 32 ? 32 : 64) * ldy * 2 < (int64_t(1) << 31); }
+bool prefill_y_fits(int64_t M, int64_t ldy) { return (M + kPB - 1) / kPB * kPB * ldy * 2 < (int64_t(1) << 31); }
 
 // Prefill launch plan: whole tiles fill whole rounds of workgroups (one per CU); the
 // tiles of a last, partial round are split along K, up to kPrefillMaxSplits ways and
@@ -1065,12 +1122,26 @@ size_t w8a8_gemm_workspace(int M, int N, int K, int kernel, int workgroups) {
 }
 
 hipError_t launch_w8a8_gemm(const W8A8Args &a, hipStream_t s) {
-    if (a.P == nullptr && use_decode(a.M, a.kernel) && decode_y_fits(a.M, a.ldy)) {
+    if (a.P != nullptr) {
+        // Partials: the kernel and plan the same call would use for y (no y, so no
+        // output-size limit, and no split reduction: each K split writes its own groups).
+        if (use_decode(a.M, a.kernel)) {
+            const DecodePlan p = decode_plan(a.M, a.N, a.K, a.workgroups);
+            if (p.m2 == 1) return launch_decode<1, true>(a, p, s);
+            return launch_decode<2, true>(a, p, s);
+        }
+        if (a.kernel != I8GS_KERNEL_TILED) {
+            const PrefillPlan p = prefill_plan(a.M, a.N, a.K);
+            const int grid = ((p.full + 7) & ~7) + (p.tiles - p.full) * p.S;
+            w8a8_prefill_partials_kernel<<<grid, 512, 0, s>>>(a.qa, a.qweight, a.M, a.N, a.K, p.full, p.S, a.P);
+            return hipGetLastError();
+        }
+    } else if (use_decode(a.M, a.kernel) && decode_y_fits(a.M, a.ldy)) {
         const DecodePlan p = decode_plan(a.M, a.N, a.K, a.workgroups);
-        if (p.m2 == 1) return launch_decode<1>(a, p, s);
-        return launch_decode<2>(a, p, s);
+        if (p.m2 == 1) return launch_decode<1, false>(a, p, s);
+        return launch_decode<2, false>(a, p, s);
     }
-    if (a.P == nullptr && a.kernel != I8GS_KERNEL_TILED && decode_y_fits(a.M, a.ldy)) {
+    if (a.P == nullptr && a.kernel != I8GS_KERNEL_TILED && prefill_y_fits(a.M, a.ldy)) {
         PrefillPlan p = prefill_plan(a.M, a.N, a.K);
         if (p.S > 1 && (a.ws == nullptr || a.ws_bytes < prefill_workspace(p) || a.counters == nullptr))
             p = {p.tiles, p.tiles, 1};  // no room for the split pieces: whole tiles only

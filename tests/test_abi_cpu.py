@@ -81,7 +81,10 @@ def _w8a8(lib, x=A, ldx=512, qa=NUL, a_s=NUL, qw=A, ws=A, y=A, ldy=256, M=8, N=2
     (dict(kernel=7), 1, "I8GS_KERNEL"),
     (dict(split=-2), 1, "decode_workgroups"),
     (dict(kernel=1, M=65), 2, "decode kernel"),
-    (dict(kernel=1, ldy=1 << 28), 2, "M*ldy*2"),
+    (dict(kernel=1, ldy=1 << 28), 2, "R*ldy*2"),
+    # 7 rows at ldy = 2^27: M*ldy*2 < 2^31, but the 32 rows the decode kernel pads to are not
+    (dict(kernel=1, M=7, ldy=1 << 27), 2, "R*ldy*2"),
+    (dict(kernel=1, M=40, ldy=(1 << 24) + 8), 2, "R*ldy*2"),
 ])
 def test_w8a8_validation(lib, kwargs, status, needle):
     rc = _w8a8(lib, **kwargs)
@@ -103,6 +106,25 @@ def test_quant_validation(lib):
     assert lib.quant_act_per_token(NUL, 512, 4, 512, A, A, NUL) == 1
     assert lib.quant_act_per_token(A, 512, 4, 512, MIS, A, NUL) == 3
     assert lib.quant_act_per_token(A, 512, 4, 0, A, A, NUL) == 2
+
+
+def test_partials_validation(lib):
+    f = lib.gemm_w8a8_g128_group_partials_ex
+    assert f(A, A, NUL, 8, 256, 512, 0, 0, NUL) == 1
+    assert f(A, A, A, 8, 256, 500, 0, 0, NUL) == 2
+    assert f(A, A, A, 8, 256, 512, 5, 0, NUL) == 1
+    assert f(A, A, A, 8, 256, 512, 0, -1, NUL) == 1
+    assert f(A, A, A, 65, 256, 512, 1, 0, NUL) == 2
+    assert "decode kernel" in lib.i8gs_last_error().decode()
+    assert f(MIS, A, A, 8, 256, 512, 0, 0, NUL) == 3
+    assert f(A, A, A, 0, 256, 512, 0, 0, NUL) == 0
+
+
+def test_w4a16_activation_offsets(lib):
+    """A chunk of up to 64 activation rows is addressed with 32-bit byte offsets."""
+    assert lib.gemm_w4a16_g128(A, 1 << 25, A, A, A, 256, 64, 256, 512, A, 1 << 30, NUL) == 2
+    assert "ldx" in lib.i8gs_last_error().decode()
+    assert lib.gemm_w4a16_g128(A, 1 << 25, A, A, A, 256, 1, 256, 512, A, 1 << 30, NUL) not in (2,)
 
 
 def test_w4a16_and_utility_validation(lib):

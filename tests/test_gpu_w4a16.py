@@ -25,6 +25,10 @@ def test_w4a16_decode_layer(layer, M):
     y_exact, T = oracle.gemm_w4a16_g128(xb, unpacked(0, f"w4-{layer}", L.K, L.N, 4), ws)
     beyond, maxulp = assert_within_tolerance(host_bf16_bits(y), y_exact, T, L.K, w4=True, what=f"w4 {layer} M={M}")
     print(f"w4a16 {layer} M={M}: {beyond} beyond a bare ulp, max {maxulp:.3f} ulp")
+    # Scaling each group's exact-product sum (not the weights) leaves only fp32 rounding of
+    # group sums and of the fold: outputs more than one bf16 unit from the exact value can
+    # only come from cancellation, at most 1 in 10^4 elements.
+    assert beyond <= max(1, y_exact.size // 10_000), (beyond, maxulp)
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 8), (8, 512, 256), (13, 384, 40), (65, 256, 136), (130, 640, 264)])

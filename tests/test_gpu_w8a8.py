@@ -21,24 +21,83 @@ def _case(seed, tag, M, K, N, outliers):
     return xb, qw, ws
 
 
-@pytest.mark.parametrize("M,K,N", [(8, 512, 256), (64, 5120, 6144), (100, 384, 72), (1, 128, 8)])
-def test_group_partials_bit_exact(M, K, N):
+# Partials come from the kernel that serves the same call: the decode kernel for M <= 64,
+# the 256 x 256 prefill kernel above (AUTO), or the 128 x 128 tiled kernel when asked for.
+KERNELS = {"auto": i8.KERNEL_AUTO, "decode": i8.KERNEL_DECODE, "tiled": i8.KERNEL_TILED}
+
+
+@pytest.mark.parametrize("M,K,N,kern", [
+    (8, 512, 256, "auto"), (8, 512, 256, "tiled"),          # the single linear
+    (1, 128, 8, "auto"), (33, 384, 72, "auto"), (64, 1024, 520, "auto"),
+    (100, 384, 72, "auto"), (100, 384, 72, "tiled"),        # prefill kernel, ragged tile
+    (300, 4096, 520, "auto"),                               # 6 tiles, K split 2 ways in the last round
+    (600, 2048, 264, "auto"),                               # 6 tiles, split 2 ways
+])
+def test_group_partials_bit_exact(M, K, N, kern):
     xb, qw, _ = _case(0, f"p{M}-{K}-{N}", M, K, N, True)
     qa, _ = oracle.quant_act_per_token(xb)
-    P = i8.gemm_w8a8_g128_group_partials(dev(qa), dev(qw))
+    P = i8.gemm_w8a8_g128_group_partials(dev(qa), dev(qw), kernel=KERNELS[kern])
     torch.cuda.synchronize()
     assert np.array_equal(P.cpu().numpy(), oracle.group_partials(qa, oracle.gptq_unpack(qw, 8, K)))
 
 
-def test_group_partials_full_code_range():
-    """Uniformly random codes (all 256, including q = -128) and random activation codes."""
-    M, K, N = 48, 1024, 96
-    words = synth.uniform_words(5, "pcodes", (K // 4) * N).reshape(K // 4, N)
-    qa = (synth.uniform_words(5, "pqa", M * K // 4).view(np.uint8).reshape(M, K).astype(np.int16) - 128)
-    qa = np.clip(qa, -127, 127).astype(np.int8)
-    P = i8.gemm_w8a8_g128_group_partials(dev(qa), dev(words))
+@pytest.mark.parametrize("wgs", [1, 3, 7, 97, 256, 10000])
+def test_group_partials_decode_splits(wgs):
+    """The decode kernel's tiles and K splits for every grid size write the same exact sums."""
+    M, K, N = 64, 5120, 512
+    xb, qw, _ = _case(2, "splits", M, K, N, True)
+    qa, _ = oracle.quant_act_per_token(xb)
+    P = i8.gemm_w8a8_g128_group_partials(dev(qa), dev(qw), kernel=i8.KERNEL_DECODE, decode_workgroups=wgs)
     torch.cuda.synchronize()
-    assert np.array_equal(P.cpu().numpy(), oracle.group_partials(qa, oracle.gptq_unpack(words, 8, K)))
+    assert np.array_equal(P.cpu().numpy(), oracle.group_partials(qa, oracle.gptq_unpack(qw, 8, K)))
+
+
+@pytest.mark.parametrize("M,K,N,kern", [(48, 1024, 96, "auto"), (48, 1024, 96, "tiled"), (5, 256, 40, "auto"),
+                                        (300, 4096, 520, "auto"), (257, 640, 264, "auto")])
+def test_group_partials_full_code_range(M, K, N, kern):
+    """Uniformly random codes (all 256, including q = -128) and random activation codes in
+    [-127, 127], through the decode kernel (M <= 64), the prefill kernel with split tiles
+    (M > 64) and the tiled kernel."""
+    words = synth.uniform_words(5, f"pcodes{M}-{K}-{N}", (K // 4) * N).reshape(K // 4, N)
+    qa = (synth.uniform_words(5, f"pqa{M}-{K}-{N}", M * K // 4).view(np.uint8).reshape(M, K).astype(np.int16) - 128)
+    qa = np.clip(qa, -127, 127).astype(np.int8)
+    q = oracle.gptq_unpack(words, 8, K)
+    assert (q == -128).any() and (q == 127).any()
+    P = i8.gemm_w8a8_g128_group_partials(dev(qa), dev(words), kernel=KERNELS[kern])
+    torch.cuda.synchronize()
+    assert np.array_equal(P.cpu().numpy(), oracle.group_partials(qa, q))
+
+
+def test_group_partials_extreme_sums():
+    """Rows of +-127 against columns of codes 0 and 255 (q = -128 and 127): group sums at the
+    ends of their range, +-127*128*128 = +-2080768, through the decode kernel's seeded
+    accumulator and the prefill kernel."""
+    K, N = 512, 64
+    q = np.full((K, N), 127, np.int16)
+    q[:, ::2] = -128
+    codes = (q + 128).astype(np.uint32).reshape(K // 4, 4, N)
+    words = (codes[:, 0] | (codes[:, 1] << 8) | (codes[:, 2] << 16) | (codes[:, 3] << 24)).view(np.int32)
+    for M in (64, 300):
+        qa = np.full((M, K), 127, np.int8)
+        qa[1::2] = -127
+        P = i8.gemm_w8a8_g128_group_partials(dev(qa), dev(words))
+        torch.cuda.synchronize()
+        ref = oracle.group_partials(qa, oracle.gptq_unpack(words, 8, K))
+        assert ref.max() == 127 * 128 * 128 and ref.min() == -127 * 128 * 128
+        assert np.array_equal(P.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("layer", ["qkv", "o_proj", "gate_up", "down"])
+def test_group_partials_decode_layer(layer):
+    """Decode workload: the exact group sums of all 64 tokens x every column, from the decode
+    kernel in the launch plan the benchmark times."""
+    L = synth.LAYERS[layer]
+    M = 64
+    xb, qw, _ = _case(0, f"decode-{layer}", M, L.K, L.N, True)
+    qa, _ = oracle.quant_act_per_token(xb)
+    P = i8.gemm_w8a8_g128_group_partials(dev(qa), dev(qw))
+    torch.cuda.synchronize()
+    assert np.array_equal(P.cpu().numpy(), oracle.group_partials(qa, unpacked(0, f"decode-{layer}", L.K, L.N, 8)))
 
 
 @pytest.mark.parametrize("layer", ["qkv", "o_proj", "gate_up", "down"])
@@ -172,7 +231,10 @@ def test_identity_probe_recovers_dequantised_rows():
 
 @pytest.mark.parametrize("layer", ["qkv", "o_proj", "gate_up", "down", "fc"])
 def test_prefill_layer_sampled_rows(layer):
-    """Prefill workload (4096 tokens): full GPU output, 24 sampled rows checked (incl. first and last)."""
+    """Prefill workload (4096 tokens): full GPU output, 24 sampled rows checked (incl. first and
+    last); the exact group sums of those rows from the prefill kernel run on all 4096 rows in
+    the benchmark's launch plan (o_proj, down and fc split their last round's tiles along K:
+    columns 4096 and up; qkv: columns 4096 and up of row tiles 8-15)."""
     L = synth.LAYERS[layer]
     M = 4096
     xb, qw, ws = _case(0, f"prefill-{layer}", M, L.K, L.N, True)
@@ -180,13 +242,16 @@ def test_prefill_layer_sampled_rows(layer):
     torch.cuda.synchronize()
     rows = synth.sample_rows(0, f"prefill-{layer}", M, 24)
     qa, s = oracle.quant_act_per_token(xb)
-    y_exact, T = oracle.gemm_w8a8_g128(qa, s, unpacked(0, f"prefill-{layer}", L.K, L.N, 8), ws, rows=rows)
+    q = unpacked(0, f"prefill-{layer}", L.K, L.N, 8)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, q, ws, rows=rows)
     yb = host_bf16_bits(y)[rows]
+    del y
     assert_within_tolerance(yb, y_exact, T, L.K, what=f"prefill {layer}")
-    # integer stage of the same rows, bit-exact
-    P = i8.gemm_w8a8_g128_group_partials(dev(qa[rows]), dev(qw))
-    torch.cuda.synchronize()
-    assert np.array_equal(P.cpu().numpy(), oracle.group_partials(qa[rows], unpacked(0, f"prefill-{layer}", L.K, L.N, 8)))
+    P = i8.gemm_w8a8_g128_group_partials(dev(qa), dev(qw))
+    Prows = P[torch.from_numpy(rows).to(P.device)].cpu().numpy()
+    del P
+    torch.cuda.empty_cache()
+    assert np.array_equal(Prows, oracle.group_partials(qa[rows], q))
 
 
 def test_lm_head_sampled_rows():
@@ -218,3 +283,41 @@ def test_strided_rows(M, K, N, kern):
     assert_within_tolerance(host_bf16_bits(yfull[:, :N].contiguous()), y_exact, T, K,
                             what=f"strided {M}x{K}x{N} kernel {kern}")
     assert bool((yfull[:, N:] == 7.0).all())
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 1024, 264), (7, 512, 256), (300, 640, 520)])
+def test_zero_activation_rows_give_zero(M, K, N):
+    """An all-zero token row has a_scale 0 and codes 0, so its output row is exactly zero
+    (decode kernel for M <= 64, prefill kernel above), the other rows as usual."""
+    xb, qw, ws = _case(6, f"zero{M}-{K}-{N}", M, K, N, True)
+    xb = xb.copy()
+    zero = [0, M // 2, M - 1]
+    xb[zero] = 0
+    y = i8.gemm_w8a8_g128(dev(qw), dev(ws), x=dev_bf16(xb))
+    torch.cuda.synchronize()
+    yf = y.float().cpu().numpy()
+    assert np.all(yf[zero] == 0.0)
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, oracle.gptq_unpack(qw, 8, K), ws)
+    assert_within_tolerance(host_bf16_bits(y), y_exact, T, K, what=f"zero rows {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M,K,N,ldy", [(7, 512, 256, 1 << 27), (40, 512, 264, (1 << 24) + 8),
+                                       (40, 512, 264, 1 << 23), (100, 384, 264, 10_000_000),
+                                       (300, 384, 264, (1 << 21) - 8)])
+def test_large_row_stride_y(M, K, N, ldy):
+    """Row strides of y near the 32-bit offset limit.  Where the rows a launch pads up to (32 or
+    64 for the decode kernel, 256 for the prefill kernel) would pass 2^31 bytes, the call takes
+    the 128 x 128 tiled kernel (64-bit addressing); below it (40 rows at 2^23, 300 rows at
+    2^21 - 8) the decode and prefill kernels drop the padded rows by their range check.  Every
+    real row holds its own result."""
+    xb, qw, ws = _case(9, f"ldy{M}-{K}-{N}", M, K, N, True)
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, oracle.gptq_unpack(qw, 8, K), ws)
+    ybuf = torch.empty(((M - 1) * ldy + N,), dtype=torch.bfloat16, device="cuda")
+    y = ybuf.as_strided((M, N), (ldy, 1))
+    i8.gemm_w8a8_g128(dev(qw), dev(ws), x=dev_bf16(xb), y=y)
+    torch.cuda.synchronize()
+    assert_within_tolerance(host_bf16_bits(y.contiguous()), y_exact, T, K, what=f"ldy={ldy} {M}x{K}x{N}")
+    del ybuf
+    torch.cuda.empty_cache()
