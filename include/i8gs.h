@@ -164,6 +164,30 @@ int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float 
                       size_t workspace_bytes, void *stream);
 
 /*
+ * gemm_w8a8_g128 for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * kernels, launch plan and results as gemm_w8a8_g128 (bit-identical y), but no
+ * workspace argument: the split-K counters, the quantised activations (when x is
+ * given) and the split-K partial sums live in a static device array of
+ * i8gs_noalloc_scratch_bytes() = 16 MiB that the library holds on every GPU it runs
+ * on until the process ends.  The call allocates and frees nothing.
+ * Limit: 64 KiB + (x given: M*K + 4*M, each rounded up to 256 bytes) + (M <= 64: the
+ * decode kernel's split pieces) must fit in 16 MiB, else I8GS_ERR_WORKSPACE and
+ * nothing is launched (every decode-sized call of the drafter layers fits; for large
+ * M pass qa/a_scale, and the prefill kernel then runs whole tiles when its split
+ * pieces do not fit).  The counters are cleared by the first call on each device
+ * (on its stream) and every completed call leaves them zero.  All calls on one GPU
+ * share its array: calls that may overlap on one GPU (different streams, threads or
+ * graphs without ordering) race and must not be issued.
+ */
+int gemm_w8a8_g128_noalloc(const void *x, int64_t ldx, const int8_t *qa, const float *a_scale,
+                           const int32_t *qweight, const float *w_scale, void *y, int64_t ldy, int64_t M,
+                           int64_t N, int64_t K, void *stream);
+
+/* Bytes of the static scratch array gemm_w8a8_g128_noalloc uses on each device. */
+size_t i8gs_noalloc_scratch_bytes(void);
+
+/*
  * The per-group int32 partials P[m, g, n] = sum_{k in group g} qa[m,k] * q[k,n]
  * of the W8A8 G128 GEMM (Qwen3.8-27B W8A8 card, "Quantization details": int8 x
  * int8 products summed per 128-wide K block), written to P (device int32

@@ -18,10 +18,12 @@ from .binding import (  # noqa: F401
     gemm_w8a8_g128,
     gemm_w8a8_g128_ex,
     gemm_w8a8_g128_group_partials,
+    gemm_w8a8_g128_noalloc,
     gptq_quantize_rtn,
     gptq_unpack,
     last_error,
     load_library,
+    noalloc_scratch_bytes,
     quant_act_per_token,
     workspace_bytes,
 )

@@ -38,7 +38,7 @@ EXPORTS = (
     "i8gs_abi_version", "i8gs_last_error", "i8gs_status_string", "quant_act_per_token",
     "i8gs_workspace_bytes", "i8gs_workspace_bytes_ex", "gemm_w8a8_g128", "gemm_w8a8_g128_ex",
     "gemm_w8a8_g128_group_partials", "gemm_w8a8_g128_group_partials_ex", "gemm_w4a16_g128", "gptq_unpack",
-    "gptq_quantize_rtn",
+    "gptq_quantize_rtn", "gemm_w8a8_g128_noalloc", "i8gs_noalloc_scratch_bytes",
 )
 
 _lib = None
@@ -80,10 +80,13 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_w8a8_g128_group_partials.argtypes = [P, P, P, I64, I64, I64, P]
     lib.gemm_w8a8_g128_group_partials_ex.argtypes = [P, P, P, I64, I64, I64, I, I, P]
     lib.gemm_w4a16_g128.argtypes = [P, I64, P, P, P, I64, I64, I64, I64, P, S, P]
+    lib.gemm_w8a8_g128_noalloc.argtypes = [P, I64, P, P, P, P, P, I64, I64, I64, I64, P]
+    lib.i8gs_noalloc_scratch_bytes.restype = S
     lib.gptq_unpack.argtypes = [P, P, I, I64, I64, P, P, P]
     lib.gptq_quantize_rtn.argtypes = [P, I, I64, I64, P, P, P]
     for name in ("quant_act_per_token", "gemm_w8a8_g128", "gemm_w8a8_g128_ex", "gemm_w8a8_g128_group_partials",
-                 "gemm_w8a8_g128_group_partials_ex", "gemm_w4a16_g128", "gptq_unpack", "gptq_quantize_rtn"):
+                 "gemm_w8a8_g128_group_partials_ex", "gemm_w4a16_g128", "gptq_unpack", "gptq_quantize_rtn",
+                 "gemm_w8a8_g128_noalloc"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -211,6 +214,35 @@ def gemm_w8a8_g128_ex(qweight: torch.Tensor, w_scale: torch.Tensor, x: Optional[
                                             _ptr(y), y.stride(0), M, N, K, kernel, decode_workgroups, _ptr(ws),
                                             0 if ws is None else ws.numel(), _stream(dev)))
     return y
+
+
+def gemm_w8a8_g128_noalloc(qweight: torch.Tensor, w_scale: torch.Tensor, y: torch.Tensor,
+                           x: Optional[torch.Tensor] = None, qa: Optional[torch.Tensor] = None,
+                           a_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gemm_w8a8_g128 through the entry point that allocates nothing (its scratch memory is a
+    static device array of the library); y must be given."""
+    _need(qweight, "qweight", torch.int32, 2)
+    _need(w_scale, "w_scale", torch.float32, 2)
+    _need(y, "y", torch.bfloat16, 2)
+    K = qweight.shape[0] * 4
+    N = qweight.shape[1]
+    if x is not None:
+        _need(x, "x", torch.bfloat16, 2)
+        M, ldx, dev = x.shape[0], x.stride(0), x.device
+    else:
+        if qa is None or a_scale is None:
+            raise ValueError("give x, or both qa and a_scale")
+        _need(qa, "qa", torch.int8, 2)
+        M, ldx, dev = qa.shape[0], 0, qa.device
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"y must be [{M}, {N}]")
+    _raise(load_library().gemm_w8a8_g128_noalloc(_ptr(x), ldx, _ptr(qa), _ptr(a_scale), _ptr(qweight),
+                                                 _ptr(w_scale), _ptr(y), y.stride(0), M, N, K, _stream(dev)))
+    return y
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load_library().i8gs_noalloc_scratch_bytes())
 
 
 def gemm_w8a8_g128(qweight, w_scale, x=None, qa=None, a_scale=None, y=None) -> torch.Tensor:

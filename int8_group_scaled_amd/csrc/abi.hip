@@ -100,11 +100,74 @@ size_t w8a8_quant_bytes(int64_t M, int64_t K) { return align256(size_t(M) * size
 
 }  // namespace
 
-#define I8GS_TRY(expr)              \
-    do {                            \
-        int _rc = (expr);           \
-        if (_rc != I8GS_OK) return _rc; \
-    } while (0)
+
+namespace i8gs {
+
+int w8a8_validate(const void *x, int64_t ldx, const int8_t *qa, const float *a_scale, const int32_t *qweight,
+                  const float *w_scale, const void *y, int64_t ldy, int64_t M, int64_t N, int64_t K, int kernel,
+                  int decode_workgroups, W8A8Plan *plan) {
+    I8GS_TRY(check_dims(M, N, K, true));
+    if (kernel < I8GS_KERNEL_AUTO || kernel > I8GS_KERNEL_TILED)
+        return fail(I8GS_ERR_INVALID_ARG, fmt("kernel=%lld is not one of I8GS_KERNEL_*", kernel));
+    if (decode_workgroups < 0)
+        return fail(I8GS_ERR_INVALID_ARG, fmt("decode_workgroups=%lld must be >= 0", decode_workgroups));
+    if (kernel == I8GS_KERNEL_DECODE && M > 64)
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("the decode kernel takes M <= 64 (M=%lld)", M));
+    const bool have_x = x != nullptr;
+    const bool have_q = qa != nullptr || a_scale != nullptr;
+    if (have_x == have_q)
+        return fail(I8GS_ERR_INVALID_ARG,
+                    "pass either x (bf16 activations) or the pre-quantised pair qa/a_scale, not both or neither");
+    plan->have_x = have_x;
+    plan->M = M;
+    plan->N = N;
+    plan->K = K;
+    plan->kernel = kernel;
+    plan->workgroups = decode_workgroups;
+    plan->quant_bytes = w8a8_quant_bytes(M, K);
+    plan->gemm_bytes = 0;
+    plan->decode = false;
+    if (M == 0 || N == 0) return I8GS_OK;
+    if (have_x) {
+        I8GS_TRY(check_ptr(x, "x"));
+        I8GS_TRY(check_ld(ldx, K, "ldx"));
+    } else {
+        I8GS_TRY(check_ptr(qa, "qa"));
+        I8GS_TRY(check_ptr(a_scale, "a_scale"));
+    }
+    I8GS_TRY(check_ptr(qweight, "qweight"));
+    I8GS_TRY(check_ptr(w_scale, "w_scale"));
+    I8GS_TRY(check_ptr(y, "y"));
+    I8GS_TRY(check_ld(ldy, N, "ldy"));
+    if (kernel == I8GS_KERNEL_DECODE && !decode_y_fits(M, ldy))
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE,
+                    fmt("the decode kernel needs R*ldy*2 < 2^31 bytes of y, R = M rounded up to 32 (M=%lld ldy=%lld)",
+                        M, ldy));
+    plan->gemm_bytes = w8a8_gemm_workspace((int)M, (int)N, (int)K, kernel, decode_workgroups);
+    plan->decode = kernel != I8GS_KERNEL_TILED && M <= 64 && decode_y_fits(M, ldy);
+    return I8GS_OK;
+}
+
+int w8a8_launch(const W8A8Plan &p, const void *x, int64_t ldx, const int8_t *qa, const float *a_scale,
+                const int32_t *qweight, const float *w_scale, void *y, int64_t ldy, char *counters, char *quant,
+                char *gemm_ws, size_t gemm_ws_bytes, hipStream_t s) {
+    if (p.have_x) {
+        int8_t *qa_ws = (int8_t *)quant;
+        float *as_ws = (float *)(quant + align256(size_t(p.M) * size_t(p.K)));
+        I8GS_TRY(hip_check(launch_quant_act((const uint16_t *)x, ldx, (int)p.M, (int)p.K, qa_ws, as_ws, s),
+                           "quant_act_per_token launch"));
+        qa = qa_ws;
+        a_scale = as_ws;
+    }
+    const bool pieces = gemm_ws != nullptr && gemm_ws_bytes > 0;
+    W8A8Args a{qa, a_scale, qweight, w_scale, (uint16_t *)y, ldy, nullptr, (int)p.M, (int)p.N, (int)p.K, p.kernel,
+               p.workgroups, pieces ? (int *)counters : nullptr, pieces ? (void *)gemm_ws : nullptr,
+               pieces ? gemm_ws_bytes : 0};
+    I8GS_TRY(hip_check(launch_w8a8_gemm(a, s), "gemm_w8a8_g128 launch"));
+    return ok();
+}
+
+}  // namespace i8gs
 
 extern "C" {
 
@@ -170,59 +233,21 @@ int gemm_w8a8_g128_ex(const void *x, int64_t ldx, const int8_t *qa, const float 
                       const int32_t *qweight, const float *w_scale, void *y, int64_t ldy, int64_t M,
                       int64_t N, int64_t K, int kernel, int decode_workgroups, void *workspace,
                       size_t workspace_bytes, void *stream) {
-    I8GS_TRY(check_dims(M, N, K, true));
-    if (kernel < I8GS_KERNEL_AUTO || kernel > I8GS_KERNEL_TILED)
-        return fail(I8GS_ERR_INVALID_ARG, fmt("kernel=%lld is not one of I8GS_KERNEL_*", kernel));
-    if (decode_workgroups < 0)
-        return fail(I8GS_ERR_INVALID_ARG, fmt("decode_workgroups=%lld must be >= 0", decode_workgroups));
-    if (kernel == I8GS_KERNEL_DECODE && M > 64)
-        return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("the decode kernel takes M <= 64 (M=%lld)", M));
-    const bool have_x = x != nullptr;
-    const bool have_q = qa != nullptr || a_scale != nullptr;
-    if (have_x == have_q)
-        return fail(I8GS_ERR_INVALID_ARG,
-                    "pass either x (bf16 activations) or the pre-quantised pair qa/a_scale, not both or neither");
+    W8A8Plan plan;
+    I8GS_TRY(w8a8_validate(x, ldx, qa, a_scale, qweight, w_scale, y, ldy, M, N, K, kernel, decode_workgroups, &plan));
     if (M == 0 || N == 0) return ok();
-    if (have_x) {
-        I8GS_TRY(check_ptr(x, "x"));
-        I8GS_TRY(check_ld(ldx, K, "ldx"));
-    } else {
-        I8GS_TRY(check_ptr(qa, "qa"));
-        I8GS_TRY(check_ptr(a_scale, "a_scale"));
-    }
-    I8GS_TRY(check_ptr(qweight, "qweight"));
-    I8GS_TRY(check_ptr(w_scale, "w_scale"));
-    I8GS_TRY(check_ptr(y, "y"));
-    I8GS_TRY(check_ld(ldy, N, "ldy"));
-    if (kernel == I8GS_KERNEL_DECODE && !decode_y_fits(M, ldy))
-        return fail(I8GS_ERR_UNSUPPORTED_SHAPE,
-                    fmt("the decode kernel needs R*ldy*2 < 2^31 bytes of y, R = M rounded up to 32 (M=%lld ldy=%lld)",
-                        M, ldy));
-    const size_t gemm_ws = w8a8_gemm_workspace((int)M, (int)N, (int)K, kernel, decode_workgroups);
-    const size_t qbytes = w8a8_quant_bytes(M, K);
-    const size_t need = kCounterBytes + qbytes + gemm_ws;
-    if (have_x || gemm_ws > 0) {
+    const size_t need = kCounterBytes + plan.quant_bytes + plan.gemm_bytes;
+    if (plan.have_x || plan.gemm_bytes > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(I8GS_ERR_WORKSPACE, fmt("workspace of %lld bytes needed, %lld given", (long long)need,
                                                  workspace ? (long long)workspace_bytes : 0LL));
         if (!aligned16(workspace)) return fail(I8GS_ERR_MISALIGNED, "workspace is not 16-byte aligned");
     }
     I8GS_TRY(check_device());
-    hipStream_t s = (hipStream_t)stream;
+    // Workspace layout: counters, the quantised activations (always counted), the split pieces.
     char *wsp = (char *)workspace;
-    if (have_x) {
-        int8_t *qa_ws = (int8_t *)(wsp + kCounterBytes);
-        float *as_ws = (float *)(wsp + kCounterBytes + align256(size_t(M) * size_t(K)));
-        I8GS_TRY(hip_check(launch_quant_act((const uint16_t *)x, ldx, (int)M, (int)K, qa_ws, as_ws, s),
-                           "quant_act_per_token launch"));
-        qa = qa_ws;
-        a_scale = as_ws;
-    }
-    W8A8Args a{qa, a_scale, qweight, w_scale, (uint16_t *)y, ldy, nullptr, (int)M, (int)N, (int)K, kernel,
-               decode_workgroups,
-               gemm_ws ? (int *)wsp : nullptr, gemm_ws ? (void *)(wsp + kCounterBytes + qbytes) : nullptr, gemm_ws};
-    I8GS_TRY(hip_check(launch_w8a8_gemm(a, s), "gemm_w8a8_g128 launch"));
-    return ok();
+    return w8a8_launch(plan, x, ldx, qa, a_scale, qweight, w_scale, y, ldy, wsp, wsp ? wsp + kCounterBytes : nullptr,
+                       wsp ? wsp + kCounterBytes + plan.quant_bytes : nullptr, plan.gemm_bytes, (hipStream_t)stream);
 }
 
 int gemm_w8a8_g128(const void *x, int64_t ldx, const int8_t *qa, const float *a_scale,

@@ -57,6 +57,32 @@ bool decode_y_fits(int64_t M, int64_t ldy);
 bool prefill_y_fits(int64_t M, int64_t ldy);
 hipError_t launch_w8a8_gemm(const W8A8Args &a, hipStream_t s);
 
+// A validated W8A8 call: what it needs and which kernel family it takes.
+struct W8A8Plan {
+    bool have_x;         // bf16 x given (quantised first), else qa / a_scale
+    bool decode;         // decode kernel (otherwise prefill or tiled)
+    size_t quant_bytes;  // quantised activations and row scales (256-byte aligned pieces)
+    size_t gemm_bytes;   // split-K pieces the GEMM kernel's plan uses (0 if none)
+    int64_t M, N, K;
+    int kernel, workgroups;
+};
+// Argument checks of gemm_w8a8_g128_ex (pure host logic, no HIP call); fills plan.
+int w8a8_validate(const void *x, int64_t ldx, const int8_t *qa, const float *a_scale, const int32_t *qweight,
+                  const float *w_scale, const void *y, int64_t ldy, int64_t M, int64_t N, int64_t K, int kernel,
+                  int decode_workgroups, W8A8Plan *plan);
+// Launches the quantisation (when x is given, into `quant`) and the GEMM.  counters:
+// kCounterBytes of split-K arrival counters, zero on entry (and on return); gemm_ws:
+// room for the split pieces (the prefill kernel runs whole tiles if it is too small).
+int w8a8_launch(const W8A8Plan &p, const void *x, int64_t ldx, const int8_t *qa, const float *a_scale,
+                const int32_t *qweight, const float *w_scale, void *y, int64_t ldy, char *counters, char *quant,
+                char *gemm_ws, size_t gemm_ws_bytes, hipStream_t s);
+
+#define I8GS_TRY(expr)                    \
+    do {                                  \
+        int _rc = (expr);                 \
+        if (_rc != I8GS_OK) return _rc;   \
+    } while (0)
+
 struct W4A16Args {
     const uint16_t *x;
     int64_t ldx;

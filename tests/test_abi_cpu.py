@@ -177,3 +177,17 @@ def test_prefill_split_workspace(lib):
     # two tiles split 4 ways; the tiled kernel needs no pieces
     assert i8.workspace_bytes(i8.OP_W8A8, 128, 512, 8192) == base(128, 8192) + 2 * 4 * piece
     assert i8.workspace_bytes(i8.OP_W8A8, 128, 512, 8192, i8.KERNEL_TILED) == base(128, 8192)
+
+
+def test_noalloc_validation(lib):
+    """The no-allocation entry point validates like gemm_w8a8_g128 and rejects, before any
+    HIP call, a call whose scratch needs exceed its 16 MiB static array."""
+    f = lib.gemm_w8a8_g128_noalloc
+    assert lib.i8gs_noalloc_scratch_bytes() == 16 << 20
+    # x given: 64 KiB + 4096*5120 quantised activations > 16 MiB
+    assert f(A, 5120, NUL, NUL, A, A, A, 256, 4096, 256, 5120, NUL) == 4
+    assert "16777216" in lib.i8gs_last_error().decode()
+    assert f(A, 512, A, A, A, A, A, 256, 8, 256, 512, NUL) == 1   # x and qa both given
+    assert f(A, 500, NUL, NUL, A, A, A, 256, 8, 256, 512, NUL) == 2
+    assert f(A, 512, NUL, NUL, A, A, MIS, 256, 8, 256, 512, NUL) == 3
+    assert f(A, 512, NUL, NUL, A, A, A, 256, 0, 256, 512, NUL) == 0
