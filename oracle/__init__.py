@@ -53,9 +53,16 @@ def _configure(lib):
     lib.oracle_bf16_from_double.restype = ctypes.c_uint16
     lib.oracle_bf16_from_double_array.argtypes = [P, I, P]
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_gemm_weight_only.argtypes = [P, I, P, P, I, I, I, I, P, I, P, P]
+    lib.oracle_gptq_quantize_rtn_group.argtypes = [P, ctypes.c_int, I, I, I, P, P]
+    lib.oracle_rmsnorm_bf16.argtypes = [P, I, P, ctypes.c_double, I, I, P]
+    lib.oracle_attn_qk_int8.argtypes = [P, P, P, P, ctypes.c_double, I, I, I, I, P, P]
+    lib.oracle_attn_pv_int8.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
     for f in ("oracle_quant_act_per_token", "oracle_gptq_unpack", "oracle_gptq_dequant",
               "oracle_gptq_quantize_rtn", "oracle_group_partials", "oracle_gemm_w8a8_g128",
-              "oracle_gemm_w4a16_g128"):
+              "oracle_gemm_w4a16_g128", "oracle_gemm_weight_only", "oracle_gptq_quantize_rtn_group",
+              "oracle_rmsnorm_bf16", "oracle_attn_qk_int8", "oracle_attn_pv_int8"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -95,6 +102,11 @@ def _check(rc: int, what: str) -> None:
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's OpenMP loops use from now on (timing of the CPU baseline)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def quant_act_per_token(x_bf16: np.ndarray):
@@ -198,3 +210,84 @@ def bf16_from_double(v: np.ndarray) -> np.ndarray:
 
 def bf16_from_double_scalar(v: float) -> int:
     return int(_load().oracle_bf16_from_double(float(v)))
+
+
+def gemm_weight_only(x_bf16, q, w_scale, group: int, rows=None):
+    """(y, T) fp64 [nrows, N]: exact weight-only output with one scale per `group` K values
+    (W8A16 at group 128 or 32; W4A16 at group 128) and its fp32 magnitude bound."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    ws = np.ascontiguousarray(w_scale, dtype=np.float32)
+    M, K = x.shape
+    N = q.shape[1]
+    r, nrows = _rows_arg(rows, M)
+    y = np.empty((nrows, N), dtype=np.float64)
+    T = np.empty((nrows, N), dtype=np.float64)
+    _check(_load().oracle_gemm_weight_only(_ptr(x), K, _ptr(q), _ptr(ws), group, M, N, K,
+                                           None if r is None else _ptr(r), nrows, _ptr(y), _ptr(T)),
+           "gemm_weight_only")
+    return y, T
+
+
+def gptq_quantize_rtn_group(w: np.ndarray, bits: int, group: int):
+    """RTN symmetric quantisation with `group` K values per scale -> (qweight int32, w_scale fp32 [K/group, N])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    K, N = w.shape
+    qw = np.empty((K // (32 // bits), N), dtype=np.int32)
+    ws = np.empty((K // group, N), dtype=np.float32)
+    _check(_load().oracle_gptq_quantize_rtn_group(_ptr(w), bits, group, K, N, _ptr(qw), _ptr(ws)), "rtn_group")
+    return qw, ws
+
+
+def rmsnorm_bf16(x_bf16, gamma_bf16, eps: float) -> np.ndarray:
+    """bf16 bit patterns [M, K] of bf16(gamma * bf16(x / sqrt(mean(x^2) + eps)))."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    g = np.ascontiguousarray(gamma_bf16, dtype=np.uint16)
+    M, K = x.shape
+    h = np.empty((M, K), dtype=np.uint16)
+    _check(_load().oracle_rmsnorm_bf16(_ptr(x), K, _ptr(g), float(eps), M, K, _ptr(h)), "rmsnorm")
+    return h
+
+
+def kv_quant_block128(kv_bf16: np.ndarray):
+    """The block-g128 INT8 KV codec: codes int8 [..., 128] and one fp32 scale per 128-wide
+    block [...], by the per-token quantiser applied to every 128-wide row."""
+    kv = np.ascontiguousarray(kv_bf16, dtype=np.uint16)
+    assert kv.shape[-1] == 128
+    lead = kv.shape[:-1]
+    qa, s = quant_act_per_token(kv.reshape(-1, 128))
+    return qa.reshape(*lead, 128), s.reshape(lead)
+
+
+def attn_qk_int8(qq, qs, kq, ks, scale: float):
+    """(s fp64 [Hq, Mq, T], dots int32 [Hq, Mq, T]) of the INT8 QK product; qq int8 [Mq, Hq, 128],
+    qs fp32 [Mq, Hq], kq int8 [T, Hkv, 128], ks fp32 [T, Hkv]."""
+    qq = np.ascontiguousarray(qq, dtype=np.int8)
+    qs = np.ascontiguousarray(qs, dtype=np.float32)
+    kq = np.ascontiguousarray(kq, dtype=np.int8)
+    ks = np.ascontiguousarray(ks, dtype=np.float32)
+    Mq, Hq, _ = qq.shape
+    T, Hkv, _ = kq.shape
+    s = np.empty((Hq, Mq, T), dtype=np.float64)
+    d = np.empty((Hq, Mq, T), dtype=np.int32)
+    _check(_load().oracle_attn_qk_int8(_ptr(qq), _ptr(qs), _ptr(kq), _ptr(ks), float(scale), Mq, T, Hq, Hkv,
+                                       _ptr(s), _ptr(d)), "attn_qk")
+    return s, d
+
+
+def attn_pv_int8(p, vq, vs):
+    """(out fp64 [Hq, Mq, 128], mag fp64 [Hq, Mq, 128], pq int8 [Hq, Mq, T], ps fp32 [Hq, Mq, ceil(T/128)])
+    of the INT8 PV product; p fp32 [Hq, Mq, T], vq int8 [T, Hkv, 128], vs fp32 [T, Hkv]."""
+    p = np.ascontiguousarray(p, dtype=np.float32)
+    vq = np.ascontiguousarray(vq, dtype=np.int8)
+    vs = np.ascontiguousarray(vs, dtype=np.float32)
+    Hq, Mq, T = p.shape
+    Hkv = vq.shape[1]
+    B = (T + 127) // 128
+    out = np.empty((Hq, Mq, 128), dtype=np.float64)
+    mag = np.empty((Hq, Mq, 128), dtype=np.float64)
+    pq = np.empty((Hq, Mq, T), dtype=np.int8)
+    ps = np.empty((Hq, Mq, B), dtype=np.float32)
+    _check(_load().oracle_attn_pv_int8(_ptr(p), _ptr(vq), _ptr(vs), Mq, T, Hq, Hkv, _ptr(out), _ptr(mag), _ptr(pq),
+                                       _ptr(ps)), "attn_pv")
+    return out, mag, pq, ps

@@ -19,8 +19,15 @@
  *  [W4]     "Qwen3.8-27B-DFlash2-W4A16-g128-sym-GPTQ" model card -- property
  *           table (W4A16, group_size 128, symmetric) and the dequant-patch
  *           table (INT32-packed GPTQ: unpack from int32 plus group scales).
- *  [W8A16]  "Qwen3.5-4B-DFlash-W8A16" model card -- RTN weight quantisation
- *           with no calibration data; the identity-probe weight recovery.
+ *  [W8A16]  "Qwen3.5-4B-DFlash-W8A16" model card -- weight-only INT8 (bf16
+ *           activations), RTN weight quantisation with no calibration data; the
+ *           identity-probe weight recovery.
+ *  [EOLE]   "qwen38/dflash2" recipe page -- quantisation settings (int8 drafter
+ *           projections are group-32 runtime RTN; int8 / int4 vocabulary heads at
+ *           group 128) and numerics (normalisation in FP32 keeping the
+ *           intermediate BF16 casts).
+ *  [FLINT serving recipe] -- the KV cache dtype int8_block_g128 and the INT8 dot
+ *           products for QK and PV.
  *
  * Readings where the pages leave a step open (each one is also listed with its
  * reason in the design notes):
@@ -35,6 +42,11 @@
  *  - synthetic weights use round-to-nearest: s = absmax / 127 (INT8) or
  *    absmax / 7 (INT4) in fp32, q = clamp(round_half_even(w / s)) to
  *    [-127, 127] or [-8, 7].
+ *  - RMS normalisation: h = bf16(gamma * bf16(x / sqrt(mean(x^2) + eps))), each
+ *    step correctly rounded in fp64 (the sum of squares exact in binary128).
+ *  - the KV codec is the per-token activation quantiser on 128-wide rows; INT8 PV
+ *    moves the V scale onto the probabilities and quantises them with the same
+ *    codec per 128-token block (the pages name INT8 PV but not this step).
  *
  * Precision: the activation quantiser and the weight quantiser run in IEEE
  * fp32 because the method fixes fp32 scales; every output value is evaluated
@@ -340,4 +352,243 @@ int oracle_num_threads(void)
 #else
     return 1;
 #endif
+}
+
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* ---------------------------------------------------------------------------
+ * Weight-only GEMM with any group size  [W8A16 card: the linear weights alone are
+ * quantised to int8 by RTN, activations stay bf16; Eole recipe, quantisation
+ * settings: the int8 drafter projections use group 32; W4 property table: 4-bit,
+ * group 128].
+ *   y[m,n] = sum_g w_s[g,n] * sum_{k in g} x[m,k] * q[k,n]
+ * with g = k / group, x the bf16 activations widened exactly and q the signed codes;
+ * T[m,n] = sum_g |w_s[g,n]| * sum_{k in g} |x[m,k] * q[k,n]|.
+ * w_scale is fp32 [K/group, N].
+ * ------------------------------------------------------------------------- */
+int oracle_gemm_weight_only(const uint16_t *x, int64_t ldx, const int8_t *q, const float *w_scale,
+                            int64_t group, int64_t M, int64_t N, int64_t K, const int64_t *rows,
+                            int64_t nrows, double *y, double *T)
+{
+    if (group <= 0 || K % group != 0 || ldx < K) return 1;
+    const int64_t G = K / group;
+    if (rows == NULL) nrows = M;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t m = rows ? rows[i] : i;
+        if (m < 0 || m >= M) { bad = 1; continue; }
+        double *acc = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double *mag = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double *ys = y + i * N;
+        double *ts = T + i * N;
+        for (int64_t n = 0; n < N; ++n) { ys[n] = 0.0; ts[n] = 0.0; }
+        for (int64_t g = 0; g < G; ++g) {
+            for (int64_t n = 0; n < N; ++n) { acc[n] = 0.0; mag[n] = 0.0; }
+            for (int64_t k = g * group; k < (g + 1) * group; ++k) {
+                double a = (double)bf16_to_float(x[m * ldx + k]);
+                const int8_t *wrow = q + k * N;
+                for (int64_t n = 0; n < N; ++n) {
+                    double p = a * (double)wrow[n];
+                    acc[n] += p;
+                    mag[n] += fabs(p);
+                }
+            }
+            const float *srow = w_scale + g * N;
+            for (int64_t n = 0; n < N; ++n) {
+                double s = (double)srow[n];
+                ys[n] += s * acc[n];
+                ts[n] += fabs(s) * mag[n];
+            }
+        }
+        free(acc);
+        free(mag);
+    }
+    return bad ? 1 : 0;
+}
+
+/* RTN symmetric weight quantisation with any group size and GPTQ packing (the same
+ * rules as oracle_gptq_quantize_rtn, with `group` consecutive K values per scale):
+ * w_scale[g, n] = absmax over the group / qmax, q = clamp(rint(w / w_scale)).
+ * w_scale is fp32 [K/group, N]  [W8A16 card: pure RTN; Eole recipe: group 32]. */
+int oracle_gptq_quantize_rtn_group(const float *w, int bits, int64_t group, int64_t K, int64_t N,
+                                   int32_t *qweight, float *w_scale)
+{
+    if (bits != 4 && bits != 8) return 1;
+    const int per = 32 / bits;
+    if (group <= 0 || K % group != 0 || group % per != 0) return 1;
+    const float qmax = bits == 8 ? 127.0f : 7.0f;
+    const float qmin = bits == 8 ? -127.0f : -8.0f;
+    const int offset = 1 << (bits - 1);
+    const int64_t G = K / group;
+    memset(qweight, 0, sizeof(int32_t) * (size_t)(K / per) * (size_t)N);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < G; ++g) {
+            float amax = 0.0f;
+            for (int64_t k = g * group; k < (g + 1) * group; ++k) {
+                float v = fabsf(w[k * N + n]);
+                if (v > amax) amax = v;
+            }
+            float s = amax / qmax;
+            w_scale[g * N + n] = s;
+            for (int64_t k = g * group; k < (g + 1) * group; ++k) {
+                float qv = 0.0f;
+                if (s != 0.0f) {
+                    qv = rintf(w[k * N + n] / s);
+                    if (qv > qmax) qv = qmax;
+                    if (qv < qmin) qv = qmin;
+                }
+                uint32_t code = (uint32_t)((int)qv + offset);
+                uint32_t *word = (uint32_t *)&qweight[(k / per) * N + n];
+                *word |= code << (bits * (int)(k % per));
+            }
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * RMS normalisation of a bf16 row, the producer of the quantised activations that
+ * feed qkv and gate/up  [W4 property table: the norms stay bf16 surfaces ahead of the
+ * quantised linears; Eole recipe, numerics: normalisation runs in FP32 with the
+ * intermediate BF16 casts preserved].  Reading: with r = 1 / sqrt(mean_k x^2 + eps),
+ *   t[m,k] = bf16(x[m,k] * r)        (the normalised value cast to bf16)
+ *   h[m,k] = bf16(gamma[k] * t[m,k]) (times the bf16 weight, cast to bf16)
+ * evaluated in fp64 with every step correctly rounded: the sum of squares is
+ * accumulated in binary128 (the squares of bf16 values are exact there, and so is
+ * their sum while the squares of a row span fewer than 2^97 binades) and rounded
+ * once to fp64; then mean = ss / K, v = mean + eps, r = 1 / sqrt(v) and x * r are
+ * single fp64 operations, and both casts round to bf16 with ties to even.  eps > 0.
+ * ------------------------------------------------------------------------- */
+int oracle_rmsnorm_bf16(const uint16_t *x, int64_t ldx, const uint16_t *gamma, double eps,
+                        int64_t M, int64_t K, uint16_t *h)
+{
+    if (K <= 0 || ldx < K || !(eps > 0.0)) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *row = x + m * ldx;
+        __float128 acc = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            __float128 v = (__float128)bf16_to_float(row[k]);
+            acc += v * v;
+        }
+        double ss = (double)acc;
+        double mean = ss / (double)K;
+        double r = 1.0 / sqrt(mean + eps);
+        for (int64_t k = 0; k < K; ++k) {
+            double v = (double)bf16_to_float(row[k]);
+            uint16_t t = oracle_bf16_from_double(v * r);
+            double prod = (double)bf16_to_float(gamma[k]) * (double)bf16_to_float(t);
+            h[m * K + k] = oracle_bf16_from_double(prod);
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * INT8 attention products on a block-g128 INT8 KV cache  [Flint card serving recipe
+ * and notes: the KV cache is "int8_block_g128" (INT8 codes with one scale per
+ * 128-wide group, i.e. per head vector of 128) for target and draft, with INT8 dot
+ * products for QK and for PV].  Codes and scales of q, k and v come from the
+ * per-token quantiser above applied to 128-wide rows (one row per token and head).
+ *
+ * QK:  s[h, i, t] = scale * qs[i, h] * ks[t, hk] * sum_d qq[i, h, d] * kq[t, hk, d]
+ * with hk = h / (Hq / Hkv) (grouped-query heads), exact in fp64.  Layouts:
+ * qq int8 [Mq, Hq, 128], qs fp32 [Mq, Hq], kq int8 [T, Hkv, 128], ks fp32 [T, Hkv],
+ * s fp64 [Hq, Mq, T]; dots (nullable) int32 [Hq, Mq, T] receives the integer dots.
+ * ------------------------------------------------------------------------- */
+int oracle_attn_qk_int8(const int8_t *qq, const float *qs, const int8_t *kq, const float *ks,
+                        double scale, int64_t Mq, int64_t T, int64_t Hq, int64_t Hkv, double *s,
+                        int32_t *dots)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0) return 1;
+    const int64_t rep = Hq / Hkv;
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < Hq; ++h) {
+        const int64_t hk = h / rep;
+        for (int64_t i = 0; i < Mq; ++i) {
+            const int8_t *qrow = qq + (i * Hq + h) * 128;
+            for (int64_t t = 0; t < T; ++t) {
+                const int8_t *krow = kq + (t * Hkv + hk) * 128;
+                int64_t dot = 0;
+                for (int d = 0; d < 128; ++d) dot += (int64_t)qrow[d] * (int64_t)krow[d];
+                const int64_t o = (h * Mq + i) * T + t;
+                s[o] = scale * (double)qs[i * Hq + h] * (double)ks[t * Hkv + hk] * (double)dot;
+                if (dots) dots[o] = (int32_t)dot;
+            }
+        }
+    }
+    return 0;
+}
+
+/* PV: for probabilities p (fp32 [Hq, Mq, T], e.g. a softmax over t) and the INT8 V
+ * cache (vq int8 [T, Hkv, 128], vs fp32 [T, Hkv]):
+ *   p'[h,i,t]   = fl32(p[h,i,t] * vs[t, hk])           (the V scale moves onto p)
+ *   ps[h,i,b]   = fl32(max_{t in block b} |p'| / 127)    (blocks of 128 tokens)
+ *   pq[h,i,t]   = clamp(rint(fl32(p' / ps)), -127, 127)   (0 where ps = 0)
+ *   out[h,i,d]  = sum_b ps[h,i,b] * sum_{t in b} pq[h,i,t] * vq[t, hk, d]   (fp64)
+ * the same group-scaled INT8 product as the linear layer, with K = tokens.  A last
+ * partial block takes its tokens only.  Reading: the pages name the INT8 PV product
+ * and the 128-wide groups but not how the probabilities are quantised; this takes the
+ * activation codec above, per 128-token block.  Outputs: out fp64 [Hq, Mq, 128],
+ * mag (the a-priori fp32 fold bound sum_b |ps| * sum_t |pq * vq|) fp64 [Hq, Mq, 128],
+ * pq int8 [Hq, Mq, T] and ps fp32 [Hq, Mq, ceil(T/128)] (both nullable). */
+int oracle_attn_pv_int8(const float *p, const int8_t *vq, const float *vs, int64_t Mq, int64_t T,
+                        int64_t Hq, int64_t Hkv, double *out, double *mag, int8_t *pq_out,
+                        float *ps_out)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0) return 1;
+    const int64_t rep = Hq / Hkv;
+    const int64_t B = (T + 127) / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t hi = 0; hi < Hq * Mq; ++hi) {
+        const int64_t h = hi / Mq, hk = h / rep;
+        const float *prow = p + hi * T;
+        double *o = out + hi * 128;
+        double *mg = mag + hi * 128;
+        for (int d = 0; d < 128; ++d) { o[d] = 0.0; mg[d] = 0.0; }
+        for (int64_t b = 0; b < B; ++b) {
+            const int64_t t0 = b * 128, t1 = t0 + 128 < T ? t0 + 128 : T;
+            float amax = 0.0f;
+            for (int64_t t = t0; t < t1; ++t) {
+                float v = fabsf(prow[t] * vs[t * Hkv + hk]);
+                if (v > amax) amax = v;
+            }
+            float ps = amax / 127.0f;
+            if (ps_out) ps_out[hi * B + b] = ps;
+            int64_t acc[128];
+            int64_t am[128];
+            for (int d = 0; d < 128; ++d) { acc[d] = 0; am[d] = 0; }
+            for (int64_t t = t0; t < t1; ++t) {
+                float pv = prow[t] * vs[t * Hkv + hk];
+                int qv = 0;
+                if (ps != 0.0f) {
+                    float r = rintf(pv / ps);
+                    if (r > 127.0f) r = 127.0f;
+                    if (r < -127.0f) r = -127.0f;
+                    qv = (int)r;
+                }
+                if (pq_out) pq_out[hi * T + t] = (int8_t)qv;
+                const int8_t *vrow = vq + (t * Hkv + hk) * 128;
+                for (int d = 0; d < 128; ++d) {
+                    acc[d] += (int64_t)qv * vrow[d];
+                    am[d] += llabs((int64_t)qv * vrow[d]);
+                }
+            }
+            for (int d = 0; d < 128; ++d) {
+                o[d] += (double)ps * (double)acc[d];
+                mg[d] += fabs((double)ps) * (double)am[d];
+            }
+        }
+    }
+    return 0;
 }

@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 import test_oracle_pins as pins
+import test_oracle_pins_next as pn
 
 MUTANTS = {
     "half-away rounding of activations": (
@@ -55,6 +56,45 @@ MUTANTS = {
     "dequant scale from the wrong group": (
         "float s = w_scale[(k / GROUP) * N + n];", "float s = w_scale[(k % 2) * N + n];",
         [lambda m: pins.test_dequant_is_rounded_product(m, 8)]),
+    "weight-only groups counted as 128 wide": (
+        "if (group <= 0 || K % group != 0 || ldx < K) return 1;\n    const int64_t G = K / group;",
+        "if (group <= 0 || K % group != 0 || ldx < K) return 1;\n    const int64_t G = K / 128;",
+        [pn.test_weight_only_group32_exact_rational]),
+    "weight-only last element of each group dropped": (
+        "for (int64_t k = g * group; k < (g + 1) * group; ++k) {\n                double a",
+        "for (int64_t k = g * group; k < (g + 1) * group - 1; ++k) {\n                double a",
+        [lambda m: pn.test_weight_only_unit_scale_is_plain_gemm(m, 32)]),
+    "rtn with groups over qmax + 1": (
+        "if (group <= 0 || K % group != 0 || group % per != 0) return 1;\n    const float qmax = bits == 8 ? 127.0f : 7.0f;",
+        "if (group <= 0 || K % group != 0 || group % per != 0) return 1;\n    const float qmax = bits == 8 ? 128.0f : 8.0f;",
+        [lambda m: pn.test_rtn_group_exact_rational(m, 8, 32)]),
+    "rmsnorm without eps": (
+        "double r = 1.0 / sqrt(mean + eps);", "double r = 1.0 / sqrt(mean);",
+        [pn.test_rmsnorm_eps_and_mean]),
+    "rmsnorm over the sum instead of the mean": (
+        "double mean = ss / (double)K;", "double mean = ss;",
+        [pn.test_rmsnorm_constant_row, pn.test_rmsnorm_eps_and_mean]),
+    "rmsnorm with one rounding instead of the bf16 cast before gamma": (
+        "uint16_t t = oracle_bf16_from_double(v * r);\n            double prod = (double)bf16_to_float(gamma[k]) * (double)bf16_to_float(t);",
+        "uint16_t t = oracle_bf16_from_double(v * r);\n            (void)t;\n            double prod = (double)bf16_to_float(gamma[k]) * (v * r);",
+        [pn.test_rmsnorm_against_decimal_square_root]),
+    "rmsnorm without gamma": (
+        "double prod = (double)bf16_to_float(gamma[k]) * (double)bf16_to_float(t);",
+        "double prod = (double)bf16_to_float(t);",
+        [pn.test_rmsnorm_constant_row]),
+    "qk grouped-query heads mapped round robin": (
+        "const int64_t hk = h / rep;", "const int64_t hk = h % Hkv;",
+        [pn.test_attn_qk_int8_brute_force]),
+    "qk dot over 127 of the 128 dimensions": (
+        "for (int d = 0; d < 128; ++d) dot += (int64_t)qrow[d] * (int64_t)krow[d];",
+        "for (int d = 0; d < 127; ++d) dot += (int64_t)qrow[d] * (int64_t)krow[d];",
+        [pn.test_attn_qk_int8_brute_force]),
+    "pv block scale taken before the V scale moves onto p": (
+        "float v = fabsf(prow[t] * vs[t * Hkv + hk]);", "float v = fabsf(prow[t]);",
+        [pn.test_attn_pv_int8_exact]),
+    "pv block scale not applied": (
+        "o[d] += (double)ps * (double)acc[d];", "o[d] += (double)acc[d];",
+        [pn.test_attn_pv_int8_exact, pn.test_attn_pv_uniform_probabilities_average_v]),
 }
 
 
