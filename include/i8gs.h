@@ -80,6 +80,7 @@ typedef enum {
 /* Operation ids for i8gs_workspace_bytes(). */
 #define I8GS_OP_W8A8 0
 #define I8GS_OP_W4A16 1
+#define I8GS_OP_WEIGHT_ONLY 2 /* gemm_weight_only (enough for any bits / group) */
 
 /* Kernel choice for gemm_w8a8_g128_ex(). */
 #define I8GS_KERNEL_AUTO 0   /* decode kernel for M <= 64, the 256x256-tile prefill kernel
@@ -223,6 +224,25 @@ int gemm_w4a16_g128(const void *x, int64_t ldx, const int32_t *qweight, const fl
                     size_t workspace_bytes, void *stream);
 
 /*
+ * Weight-only group-scaled linear, 4- or 8-bit weights (Qwen3.8-27B-DFlash2 W4A16 card,
+ * property table: 4-bit, group 128, symmetric; Qwen3.5-4B-DFlash-W8A16 card: int8
+ * weights with bf16 activations, RTN; qwen38/dflash2 recipe, quantisation settings:
+ * int8 drafter projections at group 32, int4 / int8 vocabulary heads at group 128):
+ *   y[m,n] = bf16( sum_g w_scale[g,n] * sum_{k in g} x[m,k] * q[k,n] ),  g = k / group,
+ * q = code - 2^(bits-1).  x bf16 [M, ldx]; qweight int32 [K/(32/bits), N] (code j of word
+ * [r, n] is k = (32/bits)*r + j); w_scale fp32 [K/group, N]; y bf16 [M, ldy].
+ * (bits, group) is (4, 128), (8, 128) or (8, 32); anything else is I8GS_ERR_INVALID_ARG.
+ * Weights are dequantised in registers to exact integer-valued bf16, each group is
+ * summed by bf16 MFMA in fp32 and then scaled, so y is within one bf16 unit of the
+ * exact value plus (K/group + group + 2) * 2^-24 * sum_g |w_scale| * sum_k |x*q|.
+ * Also needs (min(M,64)-1)*ldx*2 + K*2 < 2^31.  workspace:
+ * i8gs_workspace_bytes(I8GS_OP_WEIGHT_ONLY, M, N, K) bytes (may be NULL if 0).
+ */
+int gemm_weight_only(const void *x, int64_t ldx, const int32_t *qweight, int bits, const float *w_scale, int group,
+                     void *y, int64_t ldy, int64_t M, int64_t N, int64_t K, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
  * GPTQ unpack (W4A16 card dequant-patch table, "unpack from int32 plus group
  * scales"; the W8A16 card's identity probe recovers the same dense rows).
  * From qweight int32 [K/(32/bits), N] (bits = 8 or 4) write, for each output that is
@@ -243,6 +263,11 @@ int gptq_unpack(const int32_t *qweight, const float *w_scale, int bits, int64_t 
  */
 int gptq_quantize_rtn(const float *w, int bits, int64_t K, int64_t N, int32_t *qweight,
                       float *w_scale, void *stream);
+
+/* The same with `group` (32 or 128) consecutive K values per scale; w_scale is fp32
+ * [K/group, N] (qwen38/dflash2 recipe: group-32 RTN int8 projections).  Bit-exact. */
+int gptq_quantize_rtn_group(const float *w, int bits, int group, int64_t K, int64_t N, int32_t *qweight,
+                            float *w_scale, void *stream);
 
 #ifdef __cplusplus
 }

@@ -13,13 +13,16 @@ from .binding import (  # noqa: F401
     KERNEL_TILED,
     OP_W4A16,
     OP_W8A8,
+    OP_WEIGHT_ONLY,
     abi_version,
     gemm_w4a16_g128,
     gemm_w8a8_g128,
     gemm_w8a8_g128_ex,
     gemm_w8a8_g128_group_partials,
     gemm_w8a8_g128_noalloc,
+    gemm_weight_only,
     gptq_quantize_rtn,
+    gptq_quantize_rtn_group,
     gptq_unpack,
     last_error,
     load_library,

@@ -29,6 +29,7 @@ I8GS_ERR_HIP = 5
 I8GS_ERR_UNSUPPORTED_DEVICE = 6
 OP_W8A8 = 0
 OP_W4A16 = 1
+OP_WEIGHT_ONLY = 2
 KERNEL_AUTO = 0
 KERNEL_DECODE = 1
 KERNEL_TILED = 2
@@ -38,7 +39,8 @@ EXPORTS = (
     "i8gs_abi_version", "i8gs_last_error", "i8gs_status_string", "quant_act_per_token",
     "i8gs_workspace_bytes", "i8gs_workspace_bytes_ex", "gemm_w8a8_g128", "gemm_w8a8_g128_ex",
     "gemm_w8a8_g128_group_partials", "gemm_w8a8_g128_group_partials_ex", "gemm_w4a16_g128", "gptq_unpack",
-    "gptq_quantize_rtn", "gemm_w8a8_g128_noalloc", "i8gs_noalloc_scratch_bytes",
+    "gptq_quantize_rtn", "gemm_w8a8_g128_noalloc", "i8gs_noalloc_scratch_bytes", "gemm_weight_only",
+    "gptq_quantize_rtn_group",
 )
 
 _lib = None
@@ -81,12 +83,14 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_w8a8_g128_group_partials_ex.argtypes = [P, P, P, I64, I64, I64, I, I, P]
     lib.gemm_w4a16_g128.argtypes = [P, I64, P, P, P, I64, I64, I64, I64, P, S, P]
     lib.gemm_w8a8_g128_noalloc.argtypes = [P, I64, P, P, P, P, P, I64, I64, I64, I64, P]
+    lib.gemm_weight_only.argtypes = [P, I64, P, I, P, I, P, I64, I64, I64, I64, P, S, P]
+    lib.gptq_quantize_rtn_group.argtypes = [P, I, I, I64, I64, P, P, P]
     lib.i8gs_noalloc_scratch_bytes.restype = S
     lib.gptq_unpack.argtypes = [P, P, I, I64, I64, P, P, P]
     lib.gptq_quantize_rtn.argtypes = [P, I, I64, I64, P, P, P]
     for name in ("quant_act_per_token", "gemm_w8a8_g128", "gemm_w8a8_g128_ex", "gemm_w8a8_g128_group_partials",
                  "gemm_w8a8_g128_group_partials_ex", "gemm_w4a16_g128", "gptq_unpack", "gptq_quantize_rtn",
-                 "gemm_w8a8_g128_noalloc"):
+                 "gemm_w8a8_g128_noalloc", "gemm_weight_only", "gptq_quantize_rtn_group"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -315,4 +319,41 @@ def gptq_quantize_rtn(w: torch.Tensor, bits: int):
     qw = torch.empty((K // (32 // bits), N), dtype=torch.int32, device=w.device)
     ws = torch.empty((K // 128, N), dtype=torch.float32, device=w.device)
     _raise(load_library().gptq_quantize_rtn(_ptr(w), bits, K, N, _ptr(qw), _ptr(ws), _stream(w.device)))
+    return qw, ws
+
+
+def gemm_weight_only(x: torch.Tensor, qweight: torch.Tensor, w_scale: torch.Tensor, bits: int, group: int,
+                     y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Weight-only linear: bf16 x [M, K], qweight int32 [K/(32/bits), N], w_scale fp32 [K/group, N]
+    -> bf16 [M, N] (4-bit group 128, 8-bit group 32 or 128)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(qweight, "qweight", torch.int32, 2)
+    _need(w_scale, "w_scale", torch.float32, 2)
+    if not qweight.is_contiguous() or not w_scale.is_contiguous():
+        raise ValueError("qweight and w_scale must be contiguous")
+    M, K = x.shape
+    N = qweight.shape[1]
+    if bits not in (4, 8) or qweight.shape[0] * (32 // bits) != K or tuple(w_scale.shape) != (K // group, N):
+        raise ValueError(f"qweight must be [K/{32 // max(bits, 1)}, N] and w_scale [K/{group}, N]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", torch.bfloat16, 2)
+    ws = _workspace(x.device, workspace_bytes(OP_WEIGHT_ONLY, M, N, K))
+    _raise(load_library().gemm_weight_only(_ptr(x), x.stride(0), _ptr(qweight), bits, _ptr(w_scale), group, _ptr(y),
+                                           y.stride(0), M, N, K, _ptr(ws), 0 if ws is None else ws.numel(),
+                                           _stream(x.device)))
+    return y
+
+
+def gptq_quantize_rtn_group(w: torch.Tensor, bits: int, group: int):
+    """RTN symmetric quantisation of fp32 w [K, N] with `group` K values per scale ->
+    (qweight int32 [K/(32/bits), N], w_scale fp32 [K/group, N])."""
+    _need(w, "w", torch.float32, 2)
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    K, N = w.shape
+    qw = torch.empty((K // (32 // bits), N), dtype=torch.int32, device=w.device)
+    ws = torch.empty((K // group, N), dtype=torch.float32, device=w.device)
+    _raise(load_library().gptq_quantize_rtn_group(_ptr(w), bits, group, K, N, _ptr(qw), _ptr(ws),
+                                                  _stream(w.device)))
     return qw, ws

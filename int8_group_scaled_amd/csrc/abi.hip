@@ -98,6 +98,16 @@ int check_ld(int64_t ld, int64_t dim, const char *name) {
 
 size_t w8a8_quant_bytes(int64_t M, int64_t K) { return align256(size_t(M) * size_t(K)) + align256(size_t(M) * 4); }
 
+// Which kernel a 4-bit group-128 weight-only call takes: the register-streaming kernel for
+// wide layers at few tokens (the vocabulary head), where each workgroup streams long runs
+// of K, the LDS-staged W4A16 kernel on the decode layer shapes (measured faster there).
+bool wo_takes_w4(int64_t M, int64_t N) { return M <= 16 && N >= 65536; }
+
+size_t w4_or_wo_workspace(int bits, int64_t M, int64_t N, int64_t K) {
+    if (bits == 4 && !wo_takes_w4(M, N)) return w4a16_gemm_workspace((int)M, (int)N, (int)K);
+    return wo_gemm_workspace((int)M, (int)N, (int)K);
+}
+
 }  // namespace
 
 
@@ -216,10 +226,13 @@ size_t i8gs_workspace_bytes_ex(int op, int64_t M, int64_t N, int64_t K, int kern
         return kCounterBytes + w8a8_quant_bytes(M, K) +
                w8a8_gemm_workspace((int)M, (int)N, (int)K, kernel, decode_workgroups);
     }
-    if (op == I8GS_OP_W4A16) {
+    if (op == I8GS_OP_W4A16 || op == I8GS_OP_WEIGHT_ONLY) {
         if (M == 0 || N == 0) return 0;
         if (K == 0 || K % kGroup != 0) return (size_t)-1;
-        const size_t part = w4a16_gemm_workspace((int)M, (int)N, (int)K);
+        // I8GS_OP_WEIGHT_ONLY: enough for either bit width
+        const size_t part = op == I8GS_OP_W4A16 ? w4_or_wo_workspace(4, M, N, K)
+                                                : std::max(w4_or_wo_workspace(4, M, N, K),
+                                                           w4_or_wo_workspace(8, M, N, K));
         return part ? kCounterBytes + part : 0;
     }
     return (size_t)-1;
@@ -287,33 +300,7 @@ int gemm_w8a8_g128_group_partials(const int8_t *qa, const int32_t *qweight, int3
 int gemm_w4a16_g128(const void *x, int64_t ldx, const int32_t *qweight, const float *w_scale,
                     void *y, int64_t ldy, int64_t M, int64_t N, int64_t K, void *workspace,
                     size_t workspace_bytes, void *stream) {
-    I8GS_TRY(check_dims(M, N, K, true));
-    if (M == 0 || N == 0) return ok();
-    I8GS_TRY(check_ptr(x, "x"));
-    I8GS_TRY(check_ld(ldx, K, "ldx"));
-    I8GS_TRY(check_ptr(qweight, "qweight"));
-    I8GS_TRY(check_ptr(w_scale, "w_scale"));
-    I8GS_TRY(check_ptr(y, "y"));
-    I8GS_TRY(check_ld(ldy, N, "ldy"));
-    // the kernel addresses a chunk of up to 64 activation rows with 32-bit byte offsets
-    if (((std::min<int64_t>(M, 64) - 1) * ldx + K) * 2 >= (int64_t(1) << 31))
-        return fail(I8GS_ERR_UNSUPPORTED_SHAPE,
-                    fmt("the W4A16 kernel needs (min(M,64)-1)*ldx*2 + K*2 < 2^31 bytes of x (M=%lld ldx=%lld)", M,
-                        ldx));
-    const size_t part = w4a16_gemm_workspace((int)M, (int)N, (int)K);
-    const size_t need = part ? kCounterBytes + part : 0;
-    if (need > 0) {
-        if (!workspace || workspace_bytes < need)
-            return fail(I8GS_ERR_WORKSPACE, fmt("workspace of %lld bytes needed, %lld given", (long long)need,
-                                                 workspace ? (long long)workspace_bytes : 0LL));
-        if (!aligned16(workspace)) return fail(I8GS_ERR_MISALIGNED, "workspace is not 16-byte aligned");
-    }
-    I8GS_TRY(check_device());
-    char *wsp = (char *)workspace;
-    W4A16Args a{(const uint16_t *)x, ldx, qweight, w_scale, (uint16_t *)y, ldy, (int)M, (int)N, (int)K,
-                part ? (int *)wsp : nullptr, part ? (void *)(wsp + kCounterBytes) : nullptr, part};
-    I8GS_TRY(hip_check(launch_w4a16_gemm(a, (hipStream_t)stream), "gemm_w4a16_g128 launch"));
-    return ok();
+    return gemm_weight_only(x, ldx, qweight, 4, w_scale, 128, y, ldy, M, N, K, workspace, workspace_bytes, stream);
 }
 
 int gptq_unpack(const int32_t *qweight, const float *w_scale, int bits, int64_t K, int64_t N,
@@ -344,8 +331,67 @@ int gptq_quantize_rtn(const float *w, int bits, int64_t K, int64_t N, int32_t *q
     I8GS_TRY(check_ptr(qweight, "qweight"));
     I8GS_TRY(check_ptr(w_scale, "w_scale"));
     I8GS_TRY(check_device());
-    I8GS_TRY(hip_check(launch_gptq_rtn(w, bits, (int)K, (int)N, qweight, w_scale, (hipStream_t)stream),
+    I8GS_TRY(hip_check(launch_gptq_rtn(w, bits, kGroup, (int)K, (int)N, qweight, w_scale, (hipStream_t)stream),
                        "gptq_quantize_rtn launch"));
+    return ok();
+}
+
+int gptq_quantize_rtn_group(const float *w, int bits, int group, int64_t K, int64_t N, int32_t *qweight,
+                            float *w_scale, void *stream) {
+    if (bits != 4 && bits != 8) return fail(I8GS_ERR_INVALID_ARG, fmt("bits=%lld must be 4 or 8", bits));
+    if (group != 32 && group != 128) return fail(I8GS_ERR_INVALID_ARG, fmt("group=%lld must be 32 or 128", group));
+    I8GS_TRY(check_dims(0, N, K, true));
+    if (N == 0) return ok();
+    I8GS_TRY(check_ptr(w, "w"));
+    I8GS_TRY(check_ptr(qweight, "qweight"));
+    I8GS_TRY(check_ptr(w_scale, "w_scale"));
+    I8GS_TRY(check_device());
+    I8GS_TRY(hip_check(launch_gptq_rtn(w, bits, group, (int)K, (int)N, qweight, w_scale, (hipStream_t)stream),
+                       "gptq_quantize_rtn_group launch"));
+    return ok();
+}
+
+int gemm_weight_only(const void *x, int64_t ldx, const int32_t *qweight, int bits, const float *w_scale, int group,
+                     void *y, int64_t ldy, int64_t M, int64_t N, int64_t K, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    if (bits != 4 && bits != 8) return fail(I8GS_ERR_INVALID_ARG, fmt("bits=%lld must be 4 or 8", bits));
+    if (!(group == 128 || (group == 32 && bits == 8)))
+        return fail(I8GS_ERR_INVALID_ARG,
+                    fmt("group=%lld with bits=%lld: supported are 4-bit group 128 and 8-bit group 32 or 128", group,
+                        bits));
+    I8GS_TRY(check_dims(M, N, K, true));
+    if (M == 0 || N == 0) return ok();
+    I8GS_TRY(check_ptr(x, "x"));
+    I8GS_TRY(check_ld(ldx, K, "ldx"));
+    I8GS_TRY(check_ptr(qweight, "qweight"));
+    I8GS_TRY(check_ptr(w_scale, "w_scale"));
+    I8GS_TRY(check_ptr(y, "y"));
+    I8GS_TRY(check_ld(ldy, N, "ldy"));
+    // a chunk of up to 64 activation rows is addressed with 32-bit byte offsets
+    if (((std::min<int64_t>(M, 64) - 1) * ldx + K) * 2 >= (int64_t(1) << 31))
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE,
+                    fmt("the weight-only kernel needs (min(M,64)-1)*ldx*2 + K*2 < 2^31 bytes of x (M=%lld ldx=%lld)",
+                        M, ldx));
+    const size_t part = w4_or_wo_workspace(bits, M, N, K);
+    const size_t need = part ? kCounterBytes + part : 0;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(I8GS_ERR_WORKSPACE, fmt("workspace of %lld bytes needed, %lld given", (long long)need,
+                                                 workspace ? (long long)workspace_bytes : 0LL));
+        if (!aligned16(workspace)) return fail(I8GS_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    }
+    I8GS_TRY(check_device());
+    char *wsp = (char *)workspace;
+    if (bits == 4 && !wo_takes_w4(M, N)) {
+        // 4-bit group 128 on the decode shapes: the LDS-staged W4A16 kernel (faster there)
+        W4A16Args a{(const uint16_t *)x, ldx, qweight, w_scale, (uint16_t *)y, ldy, (int)M, (int)N, (int)K,
+                    part ? (int *)wsp : nullptr, part ? (void *)(wsp + kCounterBytes) : nullptr, part};
+        I8GS_TRY(hip_check(launch_w4a16_gemm(a, (hipStream_t)stream), "gemm_weight_only launch"));
+        return ok();
+    }
+    WoArgs a{(const uint16_t *)x, ldx, qweight, w_scale, (uint16_t *)y, ldy, (int)M, (int)N, (int)K, bits, group,
+             part ? (int *)wsp : nullptr, part ? (void *)(wsp + kCounterBytes) : nullptr, part};
+    I8GS_TRY(hip_check(launch_wo_gemm(a, (hipStream_t)stream), "gemm_weight_only launch"));
     return ok();
 }
 

@@ -37,9 +37,9 @@ __global__ __launch_bounds__(256) void gptq_unpack_kernel(const int32_t *__restr
     }
 }
 
-// One thread per (group g, column n).
+// One thread per (group g, column n); groups of gs consecutive K values.
 template <int BITS>
-__global__ __launch_bounds__(256) void gptq_rtn_kernel(const float *__restrict__ w, int K, int N,
+__global__ __launch_bounds__(256) void gptq_rtn_kernel(const float *__restrict__ w, int K, int N, int gs,
                                                        int32_t *__restrict__ qw, float *__restrict__ ws) {
     constexpr int PER = 32 / BITS;
     constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
@@ -49,12 +49,12 @@ __global__ __launch_bounds__(256) void gptq_rtn_kernel(const float *__restrict__
     const int n = (int)(blockIdx.x % nb) * 256 + threadIdx.x;
     const int g = (int)(blockIdx.x / nb);
     if (n >= N) return;
-    const float *col = w + (int64_t)g * kGroup * N + n;
+    const float *col = w + (int64_t)g * gs * N + n;
     float amax = 0.0f;
-    for (int i = 0; i < kGroup; ++i) amax = fmaxf(amax, fabsf(col[(int64_t)i * N]));
+    for (int i = 0; i < gs; ++i) amax = fmaxf(amax, fabsf(col[(int64_t)i * N]));
     const float s = amax / QMAX;
     ws[(int64_t)g * N + n] = s;
-    for (int wi = 0; wi < kGroup / PER; ++wi) {
+    for (int wi = 0; wi < gs / PER; ++wi) {
         uint32_t word = 0;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void gptq_rtn_kernel(const float *__restrict__
             }
             word |= (uint32_t)((int)q + OFF) << (BITS * j);
         }
-        qw[((int64_t)g * (kGroup / PER) + wi) * N + n] = (int32_t)word;
+        qw[((int64_t)g * (gs / PER) + wi) * N + n] = (int32_t)word;
     }
 }
 
@@ -82,12 +82,13 @@ hipError_t launch_gptq_unpack(const int32_t *qw, const float *ws, int bits, int 
     return hipGetLastError();
 }
 
-hipError_t launch_gptq_rtn(const float *w, int bits, int K, int N, int32_t *qw, float *ws, hipStream_t s) {
-    dim3 grid((unsigned)(((N + 255) / 256) * (int64_t)(K / kGroup))), block(256);
+hipError_t launch_gptq_rtn(const float *w, int bits, int group, int K, int N, int32_t *qw, float *ws,
+                           hipStream_t s) {
+    dim3 grid((unsigned)(((N + 255) / 256) * (int64_t)(K / group))), block(256);
     if (bits == 8)
-        gptq_rtn_kernel<8><<<grid, block, 0, s>>>(w, K, N, qw, ws);
+        gptq_rtn_kernel<8><<<grid, block, 0, s>>>(w, K, N, group, qw, ws);
     else
-        gptq_rtn_kernel<4><<<grid, block, 0, s>>>(w, K, N, qw, ws);
+        gptq_rtn_kernel<4><<<grid, block, 0, s>>>(w, K, N, group, qw, ws);
     return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ hipError_t launch_quant_act(const uint16_t *x, int64_t ldx, int M, int K, int8_t
                             float *a_scale, hipStream_t s);
 hipError_t launch_gptq_unpack(const int32_t *qw, const float *ws, int bits, int K, int N,
                               int8_t *q_out, float *w_out, hipStream_t s);
-hipError_t launch_gptq_rtn(const float *w, int bits, int K, int N, int32_t *qw, float *ws,
+hipError_t launch_gptq_rtn(const float *w, int bits, int group, int K, int N, int32_t *qw, float *ws,
                            hipStream_t s);
 
 struct W8A8Args {
@@ -96,6 +96,23 @@ struct W4A16Args {
     size_t ws_bytes;
 };
 size_t w4a16_gemm_workspace(int M, int N, int K);
+
+// Weight-only GEMM (bits 4 or 8, group 32 or 128) by the register-streaming kernel.
+struct WoArgs {
+    const uint16_t *x;
+    int64_t ldx;
+    const int32_t *qweight;
+    const float *w_scale;
+    uint16_t *y;
+    int64_t ldy;
+    int M, N, K;
+    int bits, group;
+    int *counters;
+    void *ws;
+    size_t ws_bytes;
+};
+size_t wo_gemm_workspace(int M, int N, int K);
+hipError_t launch_wo_gemm(const WoArgs &a, hipStream_t s);
 // Compute units of the current device (cached per device; 256 if unknown).
 int device_cu_count();
 hipError_t launch_w4a16_gemm(const W4A16Args &a, hipStream_t s);

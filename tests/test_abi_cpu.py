@@ -191,3 +191,22 @@ def test_noalloc_validation(lib):
     assert f(A, 500, NUL, NUL, A, A, A, 256, 8, 256, 512, NUL) == 2
     assert f(A, 512, NUL, NUL, A, A, MIS, 256, 8, 256, 512, NUL) == 3
     assert f(A, 512, NUL, NUL, A, A, A, 256, 0, 256, 512, NUL) == 0
+
+
+def test_weight_only_validation(lib):
+    f = lib.gemm_weight_only
+    # (bits, group): 4/128, 8/128 and 8/32 only
+    assert f(A, 512, A, 4, A, 32, A, 256, 8, 256, 512, A, 1 << 30, NUL) == 1
+    assert "group" in lib.i8gs_last_error().decode()
+    assert f(A, 512, A, 6, A, 128, A, 256, 8, 256, 512, A, 1 << 30, NUL) == 1
+    assert f(A, 512, A, 8, A, 64, A, 256, 8, 256, 512, A, 1 << 30, NUL) == 1
+    assert f(A, 512, A, 8, A, 32, A, 256, 8, 250, 512, A, 1 << 30, NUL) == 2
+    assert f(A, 1 << 25, A, 8, A, 32, A, 256, 64, 256, 512, A, 1 << 30, NUL) == 2
+    assert f(A, 512, A, 8, A, 32, MIS, 256, 8, 256, 512, A, 1 << 30, NUL) == 3
+    assert f(A, 512, A, 8, A, 32, A, 256, 0, 256, 512, NUL, 0, NUL) == 0
+    g = lib.gptq_quantize_rtn_group
+    assert g(A, 8, 64, 512, 256, A, A, NUL) == 1
+    assert g(A, 4, 32, 500, 256, A, A, NUL) == 2
+    import int8_group_scaled_amd as i8
+    # the weight-only workspace covers either bit width's kernel
+    assert i8.workspace_bytes(i8.OP_WEIGHT_ONLY, 64, 6144, 5120) >= i8.workspace_bytes(i8.OP_W4A16, 64, 6144, 5120)
