@@ -112,6 +112,26 @@ int quant_act_per_token(const void *x, int64_t ldx, int64_t M, int64_t K, int8_t
                         float *a_scale, void *stream);
 
 /*
+ * RMS normalisation fused with the per-token INT8 quantisation of its output, the
+ * producer of the quantised activations of the qkv and gate/up projections
+ * (Qwen3.8-27B-DFlash2-W4A16 card, bf16-surface table: the norms ahead of the quantised
+ * linears; qwen38/dflash2 recipe, numerics: FP32 normalisation keeping the intermediate
+ * BF16 casts).  For each of the M rows of x:
+ *   r = 1 / sqrt(sum_k x^2 / K + eps),  h[k] = bf16(gamma[k] * bf16(x[k] * r)),
+ *   a_scale = max |h| / 127,  qa[k] = clamp(rint(h[k] / a_scale), -127, 127)
+ * with each step correctly rounded in fp64 (the sum of squares exact), so h, qa and
+ * a_scale are bit-exact (one correct value each).
+ *   x      device bf16 [M, ldx], K % 8 == 0, ldx >= K, ldx % 8 == 0
+ *   gamma  device bf16 [K]
+ *   eps    > 0 (e.g. 1e-6)
+ *   h      device bf16 [M, K] (contiguous) or NULL: the normalised rows, output
+ *   qa     device int8 [M, K] (contiguous), output;  a_scale device fp32 [M], output
+ * K is limited to 32768 (M <= 512) or 26624 (larger M): the row stays in registers.
+ */
+int rmsnorm_quant_per_token(const void *x, int64_t ldx, const void *gamma, float eps, int64_t M, int64_t K,
+                            void *h, int8_t *qa, float *a_scale, void *stream);
+
+/*
  * Bytes of workspace gemm_w8a8_g128 (op I8GS_OP_W8A8) or gemm_w4a16_g128
  * (I8GS_OP_W4A16) needs for these sizes.  Layout: a fixed 64 KiB region of
  * split-K arrival counters at offset 0, then (W8A8) the quantised activations used

@@ -28,5 +28,6 @@ from .binding import (  # noqa: F401
     load_library,
     noalloc_scratch_bytes,
     quant_act_per_token,
+    rmsnorm_quant_per_token,
     workspace_bytes,
 )

@@ -40,7 +40,7 @@ EXPORTS = (
     "i8gs_workspace_bytes", "i8gs_workspace_bytes_ex", "gemm_w8a8_g128", "gemm_w8a8_g128_ex",
     "gemm_w8a8_g128_group_partials", "gemm_w8a8_g128_group_partials_ex", "gemm_w4a16_g128", "gptq_unpack",
     "gptq_quantize_rtn", "gemm_w8a8_g128_noalloc", "i8gs_noalloc_scratch_bytes", "gemm_weight_only",
-    "gptq_quantize_rtn_group",
+    "gptq_quantize_rtn_group", "rmsnorm_quant_per_token",
 )
 
 _lib = None
@@ -85,12 +85,14 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_w8a8_g128_noalloc.argtypes = [P, I64, P, P, P, P, P, I64, I64, I64, I64, P]
     lib.gemm_weight_only.argtypes = [P, I64, P, I, P, I, P, I64, I64, I64, I64, P, S, P]
     lib.gptq_quantize_rtn_group.argtypes = [P, I, I, I64, I64, P, P, P]
+    lib.rmsnorm_quant_per_token.argtypes = [P, I64, P, ctypes.c_float, I64, I64, P, P, P, P]
     lib.i8gs_noalloc_scratch_bytes.restype = S
     lib.gptq_unpack.argtypes = [P, P, I, I64, I64, P, P, P]
     lib.gptq_quantize_rtn.argtypes = [P, I, I64, I64, P, P, P]
     for name in ("quant_act_per_token", "gemm_w8a8_g128", "gemm_w8a8_g128_ex", "gemm_w8a8_g128_group_partials",
                  "gemm_w8a8_g128_group_partials_ex", "gemm_w4a16_g128", "gptq_unpack", "gptq_quantize_rtn",
-                 "gemm_w8a8_g128_noalloc", "gemm_weight_only", "gptq_quantize_rtn_group"):
+                 "gemm_w8a8_g128_noalloc", "gemm_weight_only", "gptq_quantize_rtn_group",
+                 "rmsnorm_quant_per_token"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -357,3 +359,21 @@ def gptq_quantize_rtn_group(w: torch.Tensor, bits: int, group: int):
     _raise(load_library().gptq_quantize_rtn_group(_ptr(w), bits, group, K, N, _ptr(qw), _ptr(ws),
                                                   _stream(w.device)))
     return qw, ws
+
+
+def rmsnorm_quant_per_token(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, want_h: bool = False,
+                            qa: Optional[torch.Tensor] = None, a_scale: Optional[torch.Tensor] = None):
+    """RMS normalisation of bf16 x [M, K] with bf16 gamma [K], fused with the per-token INT8
+    quantisation of its output -> (qa int8 [M, K], a_scale fp32 [M], h bf16 [M, K] or None)."""
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if gamma.dtype != torch.bfloat16 or tuple(gamma.shape) != (K,) or not gamma.is_contiguous() or not gamma.is_cuda:
+        raise ValueError("gamma must be a contiguous bf16 [K] tensor on the GPU")
+    if qa is None:
+        qa = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if a_scale is None:
+        a_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    h = torch.empty((M, K), dtype=torch.bfloat16, device=x.device) if want_h else None
+    _raise(load_library().rmsnorm_quant_per_token(_ptr(x), x.stride(0), _ptr(gamma), float(eps), M, K, _ptr(h),
+                                                  _ptr(qa), _ptr(a_scale), _stream(x.device)))
+    return qa, a_scale, h

@@ -217,6 +217,31 @@ int quant_act_per_token(const void *x, int64_t ldx, int64_t M, int64_t K, int8_t
     return ok();
 }
 
+int rmsnorm_quant_per_token(const void *x, int64_t ldx, const void *gamma, float eps, int64_t M, int64_t K,
+                            void *h, int8_t *qa, float *a_scale, void *stream) {
+    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim)
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("sizes must be in [0, 2^31) (M=%lld K=%lld)", M, K));
+    if (K % 8 != 0) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("K=%lld must be a multiple of 8", K));
+    if (!(eps > 0.0f) || eps > 3.0e38f) return fail(I8GS_ERR_INVALID_ARG, "eps must be positive and finite");
+    if (M == 0) return ok();
+    if (K == 0) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "K must be positive when M > 0");
+    if (K > rmsnorm_quant_max_k(M))
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE,
+                    fmt("K=%lld exceeds the %lld values a workgroup holds in registers", K, rmsnorm_quant_max_k(M)));
+    I8GS_TRY(check_ptr(x, "x"));
+    I8GS_TRY(check_ptr(gamma, "gamma"));
+    I8GS_TRY(check_ptr(qa, "qa"));
+    I8GS_TRY(check_ptr(a_scale, "a_scale"));
+    if (h) I8GS_TRY(check_ptr(h, "h"));
+    I8GS_TRY(check_ld(ldx, K, "ldx"));
+    if (int64_t(M) * ldx > (int64_t(1) << 40)) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "x too large");
+    I8GS_TRY(check_device());
+    I8GS_TRY(hip_check(launch_rmsnorm_quant((const uint16_t *)x, ldx, (const uint16_t *)gamma, (double)eps, (int)M,
+                                            (int)K, (uint16_t *)h, qa, a_scale, (hipStream_t)stream),
+                       "rmsnorm_quant_per_token launch"));
+    return ok();
+}
+
 size_t i8gs_workspace_bytes_ex(int op, int64_t M, int64_t N, int64_t K, int kernel, int decode_workgroups) {
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return (size_t)-1;
     if (op == I8GS_OP_W8A8) {

@@ -29,6 +29,9 @@ int check_device();
 // Kernel launchers (no validation; callers validate first).
 hipError_t launch_quant_act(const uint16_t *x, int64_t ldx, int M, int K, int8_t *qa,
                             float *a_scale, hipStream_t s);
+hipError_t launch_rmsnorm_quant(const uint16_t *x, int64_t ldx, const uint16_t *gamma, double eps, int M, int K,
+                                uint16_t *h, int8_t *qa, float *a_scale, hipStream_t s);
+int rmsnorm_quant_max_k(int64_t M);
 hipError_t launch_gptq_unpack(const int32_t *qw, const float *ws, int bits, int K, int N,
                               int8_t *q_out, float *w_out, hipStream_t s);
 hipError_t launch_gptq_rtn(const float *w, int bits, int group, int K, int N, int32_t *qw, float *ws,

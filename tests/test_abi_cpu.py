@@ -210,3 +210,15 @@ def test_weight_only_validation(lib):
     import int8_group_scaled_amd as i8
     # the weight-only workspace covers either bit width's kernel
     assert i8.workspace_bytes(i8.OP_WEIGHT_ONLY, 64, 6144, 5120) >= i8.workspace_bytes(i8.OP_W4A16, 64, 6144, 5120)
+
+
+def test_rmsnorm_quant_validation(lib):
+    f = lib.rmsnorm_quant_per_token
+    assert f(A, 512, A, 1e-6, 4, 500, NUL, A, A, NUL) == 2         # K % 8
+    assert f(A, 512, A, 0.0, 4, 512, NUL, A, A, NUL) == 1          # eps must be positive
+    assert f(A, 512, A, -1.0, 4, 512, NUL, A, A, NUL) == 1
+    assert f(A, 512, NUL, 1e-6, 4, 512, NUL, A, A, NUL) == 1       # gamma NULL
+    assert f(A, 512, A, 1e-6, 4, 512, MIS, A, A, NUL) == 3         # h misaligned
+    assert f(A, 40000, A, 1e-6, 4, 40000, NUL, A, A, NUL) == 2     # K past the register limit
+    assert "registers" in lib.i8gs_last_error().decode()
+    assert f(A, 512, A, 1e-6, 0, 512, NUL, A, A, NUL) == 0
