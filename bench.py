@@ -23,9 +23,15 @@ The roofline entry is for the GEMM kernel: bytes per launch K*N + 4*N*K/128 +
 M*K + 4*M (qa, a_scale) + 2*M*N, over its average duration, against 8 TB/s;
 `traffic` is the HBM bytes per launch measured with rocprofv3 counters (see
 DECODE_TRAFFIC), null when the kernel sources have changed since.
-Secondary figures: prefill (4096 tokens, five layers, GEMM kernel on
-pre-quantised activations) in TOP/s against the 5.0 POP/s dense INT8 peak, the
-W4A16 g128 sibling on the decode shapes, and the CPU oracle on the host cores.
+Secondary figures, each against its roofline: prefill (4096 tokens, five layers,
+GEMM kernel on pre-quantised activations) in TOP/s against the 5.0 POP/s dense INT8
+peak; the INT8 vocabulary head (64 tokens x 248320 columns); the weight-only GEMMs
+(W4A16 g128 and W8A16 g128 / g32 on the decode shapes at 8 and 64 tokens, and the
+INT4 / INT8 weight-only vocabulary heads at 1, 8 and 64 tokens); the RMS
+normalisation fused with the quantisation; the achievable peaks measured in the same
+run (a streaming-read kernel and an INT8 MFMA loop, libi8gs_peaks.so); clocks and
+software versions; and the CPU oracle on the host cores (the decode step, per layer,
+and single-threaded on the single linear and qkv).
 """
 from __future__ import annotations
 
@@ -70,7 +76,7 @@ def parse():
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="skip prefill and W4A16 figures")
-    ap.add_argument("--lm-head", action="store_true", help="also time the 248320-column INT8 vocabulary head")
+    ap.add_argument("--no-lm-head", action="store_true", help="skip the 248320-column vocabulary heads")
     ap.add_argument("--min-cold-bytes", type=float, default=1.0e9)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="no timing: 4 decode steps plus a 256 MiB device copy (the calibration kernel), for "
@@ -107,6 +113,70 @@ def linear_bytes(M, K, N):
 
 def w4_bytes(M, K, N):
     return K * N // 2 + 4 * N * K // 128 + 2 * M * K + 2 * M * N
+
+
+def wo_bytes(M, K, N, bits, group):
+    """Weight-only GEMM: codes, fp32 scales, bf16 x in, bf16 y out."""
+    return K * N * bits // 8 + 4 * N * K // group + 2 * M * K + 2 * M * N
+
+
+def environment():
+    """Software versions and the GPU clocks (rocm-smi) at the time of the call."""
+    import subprocess
+
+    import torch
+    env = {"torch": torch.__version__, "hip": torch.version.hip, "device": torch.cuda.get_device_name(0)}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        card = next(iter(json.loads(r.stdout).values()))
+        env["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower() or k.lower().startswith(("sclk", "mclk", "fclk"))}
+    except Exception as e:  # rocm-smi absent or not parseable: report why
+        env["clocks"] = f"unavailable ({type(e).__name__})"
+    return env
+
+
+def measured_peaks(torch, dev):
+    """Achievable HBM read bandwidth and dense INT8 MFMA rate on this GPU, from the
+    in-repo microbenchmarks (libi8gs_peaks.so), timed with HIP events on the current stream."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "int8_group_scaled_amd", "libi8gs_peaks.so"))
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.i8gs_peak_stream_read.argtypes = [P, S, P, I, P]
+    lib.i8gs_peak_mfma_i8.argtypes = [I, P, I, P]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = cus * 8
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    nbytes = 4 << 30  # 4 GiB: far beyond the 256 MB last-level cache
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(f, reps):
+        f()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t = run(lambda: lib.i8gs_peak_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                              ctypes.c_void_p(sink.data_ptr()), blocks, stream), 5)
+    hbm = nbytes / t / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    iters = 4096
+    t = run(lambda: lib.i8gs_peak_mfma_i8(iters, ctypes.c_void_p(sink.data_ptr()), blocks, stream), 3)
+    tops = blocks * 4 * iters * 4 * 65536 / t / 1e12
+    return {"hbm_read_GBps": round(hbm, 1), "int8_mfma_TOPS": round(tops, 1),
+            "kernels": "i8gs_peak_stream_read (4 GiB, 16-byte non-temporal loads), "
+                       "i8gs_peak_mfma_i8 (4 independent v_mfma_i32_32x32x32_i8 chains per wave)"}
 
 
 class Timer:
@@ -357,27 +427,100 @@ def main():
             torch.cuda.empty_cache()
         out["w4a16"] = w4
 
-    if args.lm_head:
-        L = synth.LAYERS["lm_head"]
-        xb = synth.activations_bf16(0, "bench-lm", M, L.K, outliers=False)
+    def timed(key, calls, reps):
+        """Average event-timed duration (us) of reps launches, cycling through calls."""
+        for c in calls[:2]:
+            c()
+        torch.cuda.synchronize()
+        spin(torch, 5)
+        for r in range(reps):
+            e0 = timer.mark()
+            calls[r % len(calls)]()
+            e1 = timer.mark()
+            timer.add(key, e0, e1)
+        torch.cuda.synchronize()
+        return timer.mean_us(key)[0]
+
+    def cold_copies(t_pair, nbytes):
+        reps = max(2, math.ceil(args.min_cold_bytes / nbytes))
+        return [t_pair] + [tuple(t.clone() for t in t_pair) for _ in range(reps - 1)]
+
+    if not args.no_extras:
+        # ---------------- W8A16 (weight-only INT8) at group 128 and 32 on the decode shapes
+        w8 = {}
+        for L in layers:
+            w = torch.from_numpy(synth.weights_f32(0, f"bench-w8-{L.name}", L.K, L.N)).to(dev)
+            for group in (128, 32):
+                qw, sc = i8.gptq_quantize_rtn_group(w, 8, group)
+                copies = cold_copies((qw, sc), qw.numel() * 4)
+                for Mw in (8, 64):
+                    xb = synth.activations_bf16(0, f"bench-w8-{L.name}-{Mw}", Mw, L.K, outliers=True)
+                    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+                    y = torch.empty((Mw, L.N), dtype=torch.bfloat16, device=dev)
+                    calls = [lambda c=c: i8.gemm_weight_only(x, c[0], c[1], 8, group, y) for c in copies]
+                    gm = timed(("w8", L.name, group, Mw), calls, 50)
+                    b = wo_bytes(Mw, L.K, L.N, 8, group)
+                    w8[f"{L.name}_g{group}_M{Mw}"] = {"us": round(gm, 3), "GBps": round(b / (gm * 1e-6) / 1e9, 1),
+                                                      "frac_hbm": round(b / (gm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                del copies, qw, sc
+            del w
+            torch.cuda.empty_cache()
+        out["w8a16"] = w8
+
+        # ---------------- RMS normalisation fused with the quantisation (decode: 64 x 5120)
+        xb = synth.activations_bf16(0, "bench-rms", M, 5120, outliers=True)
         x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+        gamma = torch.ones(5120, dtype=torch.bfloat16, device=dev)
+        qa_b = torch.empty((M, 5120), dtype=torch.int8, device=dev)
+        s_b = torch.empty((M,), dtype=torch.float32, device=dev)
+        us_f = timed(("rmsq",), [lambda: i8.rmsnorm_quant_per_token(x, gamma, 1e-6, qa=qa_b, a_scale=s_b)], 50)
+        us_q = timed(("q5120",), [lambda: i8.quant_act_per_token(x, qa_b, s_b)], 50)
+        out["rmsnorm_quant"] = {"M": M, "K": 5120, "fused_us": round(us_f, 3), "quant_only_us": round(us_q, 3),
+                                "bytes": 2 * M * 5120 + 2 * 5120 + M * 5120 + 4 * M,
+                                "note": "one launch per layer input in place of a normalisation kernel "
+                                        "followed by the quantisation kernel"}
+
+    if not args.no_lm_head:
+        # ---------------- vocabulary heads: 248320 columns (naturally cold: 0.64-1.27 GB of codes)
+        L = synth.LAYERS["lm_head"]
+        heads = {}
         w = torch.from_numpy(synth.weights_f32(0, "bench-lm", L.K, L.N)).to(dev)
         qw, sc = i8.gptq_quantize_rtn(w, 8)
-        del w
-        qa, s = i8.quant_act_per_token(x)
+        xb = synth.activations_bf16(0, "bench-lm", M, L.K, outliers=False)
+        x64 = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+        qa, s = i8.quant_act_per_token(x64)
         y = torch.empty((M, L.N), dtype=torch.bfloat16, device=dev)
-        i8.gemm_w8a8_g128(qw, sc, qa=qa, a_scale=s, y=y)
-        torch.cuda.synchronize()
-        for _ in range(20):
-            e0 = timer.mark()
-            i8.gemm_w8a8_g128(qw, sc, qa=qa, a_scale=s, y=y)
-            e1 = timer.mark()
-            timer.add(("lm",), e0, e1)
-        torch.cuda.synchronize()
-        gm, _, _ = timer.mean_us(("lm",))
+        gm = timed(("lm",), [lambda: i8.gemm_w8a8_g128(qw, sc, qa=qa, a_scale=s, y=y)], 20)
         b = gemm_bytes(M, L.K, L.N)
-        out["lm_head"] = {"us": round(gm, 2), "GBps": round(b / (gm * 1e-6) / 1e9, 1),
-                          "frac_hbm": round(b / (gm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        heads["w8a8_M64"] = {"us": round(gm, 2), "GBps": round(b / (gm * 1e-6) / 1e9, 1),
+                             "frac_hbm": round(b / (gm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                             "kernel": "w8a8_decode_kernel"}
+        out["lm_head"] = heads["w8a8_M64"]
+        for bits in (4, 8):
+            qw2, sc2 = (i8.gptq_quantize_rtn(w, 4) if bits == 4 else (qw, sc))
+            for Mw in (1, 8, 64):
+                xw = x64[:Mw].contiguous()
+                yw = torch.empty((Mw, L.N), dtype=torch.bfloat16, device=dev)
+                gm = timed(("lmw", bits, Mw), [lambda: i8.gemm_weight_only(xw, qw2, sc2, bits, 128, yw)], 20)
+                b = wo_bytes(Mw, L.K, L.N, bits, 128)
+                heads[f"w{bits}a16_M{Mw}"] = {"us": round(gm, 2), "GBps": round(b / (gm * 1e-6) / 1e9, 1),
+                                              "frac_hbm": round(b / (gm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            del qw2, sc2
+        out["vocab_heads"] = heads
+        del w, qw, sc, x64, qa, s, y
+        torch.cuda.empty_cache()
+        log(f"vocabulary heads: " + ", ".join(f"{k} {v['GBps']:.0f} GB/s" for k, v in heads.items()))
+
+    # ---------------- measured ceilings and environment
+    peaks = measured_peaks(torch, dev)
+    out["measured_peaks"] = peaks
+    out["roofline"]["measured_peak"] = peaks["hbm_read_GBps"]
+    out["roofline"]["frac_of_measured_peak"] = round(achieved / peaks["hbm_read_GBps"], 4)
+    if "prefill" in out:
+        out["prefill"]["measured_peak_TOPS"] = peaks["int8_mfma_TOPS"]
+        out["prefill"]["frac_of_measured_peak"] = round(out["prefill"]["TOPS"] / peaks["int8_mfma_TOPS"], 4)
+    out["environment"] = environment()
+    log(f"measured peaks: {peaks['hbm_read_GBps']:.0f} GB/s HBM read, {peaks['int8_mfma_TOPS']:.0f} TOP/s INT8 MFMA")
 
     # ---------------- CPU oracle baseline (rank 0, N=1 only)
     if not args.no_cpu:
@@ -390,24 +533,53 @@ def main():
             w = synth.weights_f32(0, f"bench-decode-{L.name}", L.K, L.N)
             qw, sc = oracle.gptq_quantize_rtn(w, 8)
             host.append((xb, qw, sc, L))
+
+        def oracle_linear(xb, qw, sc, L):
+            qa, s = oracle.quant_act_per_token(xb)
+            q = oracle.gptq_unpack(qw, 8, L.K)
+            yex, _ = oracle.gemm_w8a8_g128(qa, s, q, sc)
+            oracle.bf16_from_double(yex)
+
+        per = {L.name: 0.0 for L in layers}
         reps = 0
         t0 = time.perf_counter()
         while True:
             for xb, qw, sc, L in host:
-                qa, s = oracle.quant_act_per_token(xb)
-                q = oracle.gptq_unpack(qw, 8, L.K)
-                yex, _ = oracle.gemm_w8a8_g128(qa, s, q, sc)
-                oracle.bf16_from_double(yex)
+                ta = time.perf_counter()
+                oracle_linear(xb, qw, sc, L)
+                per[L.name] += time.perf_counter() - ta
             reps += 1
             el = time.perf_counter() - t0
             if el >= 10.0 or reps >= 50:
                 break
         cpu_gbs = step_bytes * reps / el / 1e9
-        out["cpu_baseline"] = {"value": round(cpu_gbs, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+        threads = oracle.num_threads()
+        per_layer_cpu = {L.name: round(linear_bytes(M, L.K, L.N) * reps / per[L.name] / 1e9, 3) for L in layers}
+        # single-threaded: the single linear (8 x 512 x 256) and the decode qkv layer
+        oracle.set_num_threads(1)
+        xs = synth.activations_bf16(0, "bench-single", 8, 512, outliers=False)
+        qws, scs = oracle.gptq_quantize_rtn(synth.weights_f32(0, "bench-single", 512, 256), 8)
+        single = synth.LAYERS["single"]
+        ta = time.perf_counter()
+        n_single = 0
+        while time.perf_counter() - ta < 1.0:
+            oracle_linear(xs, qws, scs, single)
+            n_single += 1
+        t_single = (time.perf_counter() - ta) / n_single
+        xb, qw, sc, L = host[0]
+        ta = time.perf_counter()
+        oracle_linear(xb, qw, sc, L)
+        t_qkv = time.perf_counter() - ta
+        oracle.set_num_threads(threads)
+        out["cpu_baseline"] = {"value": round(cpu_gbs, 3), "unit": "GB/s", "cores": threads,
                                "kind": "oracle",
                                "sample": f"the full decode step (64 tokens x 4 layers: quantise, unpack, exact "
-                                         f"group sums, fold, bf16) repeated {reps}x in {el:.1f}s"}
-        log(f"cpu oracle: {cpu_gbs:.2f} GB/s on {oracle.num_threads()} threads")
+                                         f"group sums, fold, bf16) repeated {reps}x in {el:.1f}s",
+                               "per_layer_GBps": per_layer_cpu,
+                               "single_thread": {"single_linear_8x512x256_ms": round(t_single * 1e3, 3),
+                                                 "qkv_64x5120x6144_s": round(t_qkv, 3)}}
+        log(f"cpu oracle: {cpu_gbs:.2f} GB/s on {threads} threads; single thread: single linear "
+            f"{t_single * 1e3:.2f} ms, qkv {t_qkv:.2f} s")
 
     print(json.dumps(out), flush=True)
 
