@@ -289,6 +289,62 @@ int gptq_quantize_rtn(const float *w, int bits, int64_t K, int64_t N, int32_t *q
 int gptq_quantize_rtn_group(const float *w, int bits, int group, int64_t K, int64_t N, int32_t *qweight,
                             float *w_scale, void *stream);
 
+/*
+ * INT8 block-g128 KV cache codec (Flint-DFlash2-GPTQ-INT8-PTQR model card, serving
+ * recipe: the target's and the draft's KV cache dtype "int8_block_g128"; serving notes).
+ * One fp32 scale per 128-wide group, i.e. per head vector of one token, with the
+ * per-token activation quantiser applied to each such vector:
+ *   scales[t, h] = max_d |kv[t, h, d]| / 127 (fp32),
+ *   codes[t, h, d] = clamp(rint(kv[t, h, d] / scales[t, h]), -127, 127)   (ties to even)
+ *   kv      device bf16, head vector h of token t at kv + t*ld + 128*h (ld >= 128*H,
+ *           ld % 8 == 0): a contiguous [T, H, 128] cache, or the K or V slice of a fused
+ *           qkv projection output (pointer at the slice, ld = the output's row length)
+ *   codes   device int8 [T, H, 128], output;  scales  device fp32 [T, H], output
+ * Bit-exact.  The query side of the QK product quantises its head vectors the same way.
+ */
+int kv_quant_int8_block128(const void *kv, int64_t ld, int64_t T, int64_t H, int8_t *codes, float *scales,
+                           void *stream);
+
+/*
+ * INT8 QK product on the block-g128 cache (Flint card serving recipe: INT8 DOT
+ * attention on the int8_block_g128 KV cache).  For Hq query heads sharing Hkv KV heads
+ * (head h reads KV head h / (Hq/Hkv)) and head dimension 128:
+ *   dots[h, i, t] = sum_d qq[i, h, d] * kq[t, hk, d]     (exact int32)
+ *   s[h, i, t]    = ((scale * qs[i, h]) * ks[t, hk]) * dots[h, i, t]   (fp32, in this order)
+ * so s is within 3 * 2^-24 relative of the exact product of the four factors (the
+ * int32 dot converts exactly: |dot| <= 128 * 127^2 < 2^24).
+ *   qq int8 [Mq, Hq, 128], qs fp32 [Mq, Hq] (the codec's output for the queries)
+ *   kq int8 [T, Hkv, 128], ks fp32 [T, Hkv] (the K cache)
+ *   scale   finite fp32 (e.g. 1/sqrt(128))
+ *   s       fp32 [Hq, Mq, T], output;  dots  int32 [Hq, Mq, T] or NULL, output
+ * Hq % Hkv == 0, Hkv > 0, Hq <= 65535, Mq <= 1048560, Hq*Mq*T <= 2^40.  Empty sizes
+ * are a no-op.
+ */
+int attn_qk_int8(const int8_t *qq, const float *qs, const int8_t *kq, const float *ks, float scale, int64_t Mq,
+                 int64_t T, int64_t Hq, int64_t Hkv, float *s, int32_t *dots, void *stream);
+
+/*
+ * INT8 PV product on the block-g128 cache (Flint card serving recipe: INT8 PV).  The
+ * pages name the INT8 PV product but not how the probabilities are quantised; this
+ * moves each token's V scale onto its probability and quantises the result per block
+ * of 128 tokens with the activation codec, so the product is the group-scaled INT8
+ * product of the linear layer with K = tokens:
+ *   p'[h,i,t]  = fl32(p[h,i,t] * vs[t, hk])
+ *   ps[h,i,b]  = max_{t in block b} |p'| / 127  (fp32; a last partial block takes its tokens)
+ *   pq[h,i,t]  = clamp(rint(p' / ps), -127, 127)  (0 where ps = 0; IEEE division)
+ *   out[h,i,d] = sum_b ps[h,i,b] * sum_{t in b} pq[h,i,t] * vq[t, hk, d]
+ * The block sums are exact int32; the fold over blocks is fp32, so out is within
+ * (B + 2) * 2^-24 * sum_b |ps| * sum_t |pq * vq| of the exact value (B = ceil(T/128)).
+ * pq and ps are bit-exact.
+ *   p   fp32 [Hq, Mq, T] (e.g. softmax of the QK scores);  vq int8 [T, Hkv, 128],
+ *   vs  fp32 [T, Hkv] (the V cache)
+ *   out fp32 [Hq, Mq, 128], output (zeros when T == 0)
+ *   pq  int8 [Hq, Mq, T] or NULL;  ps  fp32 [Hq, Mq, B] or NULL (outputs)
+ * Size limits as for attn_qk_int8.
+ */
+int attn_pv_int8(const float *p, const int8_t *vq, const float *vs, int64_t Mq, int64_t T, int64_t Hq, int64_t Hkv,
+                 float *out, int8_t *pq, float *ps, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,6 +15,8 @@ from .binding import (  # noqa: F401
     OP_W8A8,
     OP_WEIGHT_ONLY,
     abi_version,
+    attn_pv_int8,
+    attn_qk_int8,
     gemm_w4a16_g128,
     gemm_w8a8_g128,
     gemm_w8a8_g128_ex,
@@ -24,6 +26,7 @@ from .binding import (  # noqa: F401
     gptq_quantize_rtn,
     gptq_quantize_rtn_group,
     gptq_unpack,
+    kv_quant_int8_block128,
     last_error,
     load_library,
     noalloc_scratch_bytes,

@@ -40,7 +40,8 @@ EXPORTS = (
     "i8gs_workspace_bytes", "i8gs_workspace_bytes_ex", "gemm_w8a8_g128", "gemm_w8a8_g128_ex",
     "gemm_w8a8_g128_group_partials", "gemm_w8a8_g128_group_partials_ex", "gemm_w4a16_g128", "gptq_unpack",
     "gptq_quantize_rtn", "gemm_w8a8_g128_noalloc", "i8gs_noalloc_scratch_bytes", "gemm_weight_only",
-    "gptq_quantize_rtn_group", "rmsnorm_quant_per_token",
+    "gptq_quantize_rtn_group", "rmsnorm_quant_per_token", "kv_quant_int8_block128", "attn_qk_int8",
+    "attn_pv_int8",
 )
 
 _lib = None
@@ -87,12 +88,15 @@ def load_library(path: str = LIB_PATH):
     lib.gptq_quantize_rtn_group.argtypes = [P, I, I, I64, I64, P, P, P]
     lib.rmsnorm_quant_per_token.argtypes = [P, I64, P, ctypes.c_float, I64, I64, P, P, P, P]
     lib.i8gs_noalloc_scratch_bytes.restype = S
+    lib.kv_quant_int8_block128.argtypes = [P, I64, I64, I64, P, P, P]
+    lib.attn_qk_int8.argtypes = [P, P, P, P, ctypes.c_float, I64, I64, I64, I64, P, P, P]
+    lib.attn_pv_int8.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, P]
     lib.gptq_unpack.argtypes = [P, P, I, I64, I64, P, P, P]
     lib.gptq_quantize_rtn.argtypes = [P, I, I64, I64, P, P, P]
     for name in ("quant_act_per_token", "gemm_w8a8_g128", "gemm_w8a8_g128_ex", "gemm_w8a8_g128_group_partials",
                  "gemm_w8a8_g128_group_partials_ex", "gemm_w4a16_g128", "gptq_unpack", "gptq_quantize_rtn",
                  "gemm_w8a8_g128_noalloc", "gemm_weight_only", "gptq_quantize_rtn_group",
-                 "rmsnorm_quant_per_token"):
+                 "rmsnorm_quant_per_token", "kv_quant_int8_block128", "attn_qk_int8", "attn_pv_int8"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -377,3 +381,78 @@ def rmsnorm_quant_per_token(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1
     _raise(load_library().rmsnorm_quant_per_token(_ptr(x), x.stride(0), _ptr(gamma), float(eps), M, K, _ptr(h),
                                                   _ptr(qa), _ptr(a_scale), _stream(x.device)))
     return qa, a_scale, h
+
+
+def _need_c(t: torch.Tensor, name: str, dtype, shape):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous() \
+            or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on the GPU")
+
+
+def kv_quant_int8_block128(kv: torch.Tensor, heads: Optional[int] = None, codes: Optional[torch.Tensor] = None,
+                           scales: Optional[torch.Tensor] = None):
+    """INT8 block-g128 codec of a KV slice: bf16 kv [T, H, 128] (contiguous), or bf16
+    [T, >= 128*heads] whose first 128*heads values per row are the H head vectors (e.g.
+    a column slice of a fused qkv output) -> (codes int8 [T, H, 128], scales fp32 [T, H])."""
+    if not isinstance(kv, torch.Tensor) or kv.dtype != torch.bfloat16 or not kv.is_cuda:
+        raise ValueError("kv must be a bf16 tensor on the GPU")
+    if kv.dim() == 3:
+        if kv.shape[2] != 128 or kv.stride(2) != 1 or kv.stride(1) != 128:
+            raise ValueError("kv [T, H, 128] must have contiguous head vectors")
+        T, H, ld = kv.shape[0], kv.shape[1], kv.stride(0)
+    elif kv.dim() == 2:
+        if heads is None or kv.stride(1) != 1 or kv.shape[1] < 128 * heads:
+            raise ValueError("a 2-D kv needs heads and rows of at least 128*heads contiguous values")
+        T, H, ld = kv.shape[0], int(heads), kv.stride(0)
+    else:
+        raise ValueError("kv must be [T, H, 128] or [T, 128*H]")
+    if codes is None:
+        codes = torch.empty((T, H, 128), dtype=torch.int8, device=kv.device)
+    if scales is None:
+        scales = torch.empty((T, H), dtype=torch.float32, device=kv.device)
+    _need_c(codes, "codes", torch.int8, (T, H, 128))
+    _need_c(scales, "scales", torch.float32, (T, H))
+    _raise(load_library().kv_quant_int8_block128(_ptr(kv), ld, T, H, _ptr(codes), _ptr(scales), _stream(kv.device)))
+    return codes, scales
+
+
+def attn_qk_int8(qq: torch.Tensor, qs: torch.Tensor, kq: torch.Tensor, ks: torch.Tensor, scale: float,
+                 want_dots: bool = False, s: Optional[torch.Tensor] = None):
+    """INT8 QK scores on the block-g128 cache: qq int8 [Mq, Hq, 128], qs fp32 [Mq, Hq],
+    kq int8 [T, Hkv, 128], ks fp32 [T, Hkv] -> (s fp32 [Hq, Mq, T], dots int32 or None)."""
+    if qq.dim() != 3 or kq.dim() != 3:
+        raise ValueError("qq and kq must be [rows, heads, 128]")
+    Mq, Hq, T, Hkv = qq.shape[0], qq.shape[1], kq.shape[0], kq.shape[1]
+    _need_c(qq, "qq", torch.int8, (Mq, Hq, 128))
+    _need_c(qs, "qs", torch.float32, (Mq, Hq))
+    _need_c(kq, "kq", torch.int8, (T, Hkv, 128))
+    _need_c(ks, "ks", torch.float32, (T, Hkv))
+    if s is None:
+        s = torch.empty((Hq, Mq, T), dtype=torch.float32, device=qq.device)
+    _need_c(s, "s", torch.float32, (Hq, Mq, T))
+    dots = torch.empty((Hq, Mq, T), dtype=torch.int32, device=qq.device) if want_dots else None
+    _raise(load_library().attn_qk_int8(_ptr(qq), _ptr(qs), _ptr(kq), _ptr(ks), float(scale), Mq, T, Hq, Hkv,
+                                       _ptr(s), _ptr(dots), _stream(qq.device)))
+    return s, dots
+
+
+def attn_pv_int8(p: torch.Tensor, vq: torch.Tensor, vs: torch.Tensor, want_codes: bool = False,
+                 out: Optional[torch.Tensor] = None):
+    """INT8 PV on the block-g128 cache: p fp32 [Hq, Mq, T], vq int8 [T, Hkv, 128], vs fp32
+    [T, Hkv] -> (out fp32 [Hq, Mq, 128], pq int8 [Hq, Mq, T] or None, ps fp32 [Hq, Mq, B] or None)."""
+    if p.dim() != 3 or vq.dim() != 3:
+        raise ValueError("p must be [Hq, Mq, T] and vq [T, Hkv, 128]")
+    Hq, Mq, T = p.shape
+    Hkv = vq.shape[1]
+    _need_c(p, "p", torch.float32, (Hq, Mq, T))
+    _need_c(vq, "vq", torch.int8, (T, Hkv, 128))
+    _need_c(vs, "vs", torch.float32, (T, Hkv))
+    if out is None:
+        out = torch.empty((Hq, Mq, 128), dtype=torch.float32, device=p.device)
+    _need_c(out, "out", torch.float32, (Hq, Mq, 128))
+    B = (T + 127) // 128
+    pq = torch.empty((Hq, Mq, T), dtype=torch.int8, device=p.device) if want_codes else None
+    ps = torch.empty((Hq, Mq, B), dtype=torch.float32, device=p.device) if want_codes else None
+    _raise(load_library().attn_pv_int8(_ptr(p), _ptr(vq), _ptr(vs), Mq, T, Hq, Hkv, _ptr(out), _ptr(pq), _ptr(ps),
+                                       _stream(p.device)))
+    return out, pq, ps

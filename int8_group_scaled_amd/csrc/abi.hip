@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -61,9 +62,9 @@ constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-std::string fmt(const char *f, long long a, long long b = 0, long long c = 0) {
+std::string fmt(const char *f, long long a, long long b = 0, long long c = 0, long long d = 0) {
     char buf[256];
-    snprintf(buf, sizeof buf, f, a, b, c);
+    snprintf(buf, sizeof buf, f, a, b, c, d);
     return buf;
 }
 
@@ -417,6 +418,75 @@ int gemm_weight_only(const void *x, int64_t ldx, const int32_t *qweight, int bit
     WoArgs a{(const uint16_t *)x, ldx, qweight, w_scale, (uint16_t *)y, ldy, (int)M, (int)N, (int)K, bits, group,
              part ? (int *)wsp : nullptr, part ? (void *)(wsp + kCounterBytes) : nullptr, part};
     I8GS_TRY(hip_check(launch_wo_gemm(a, (hipStream_t)stream), "gemm_weight_only launch"));
+    return ok();
+}
+
+int kv_quant_int8_block128(const void *kv, int64_t ld, int64_t T, int64_t H, int8_t *codes, float *scales,
+                           void *stream) {
+    if (T < 0 || H < 0 || T > kMaxDim || H > kMaxDim || ld < 0)
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("sizes must be in [0, 2^31) (T=%lld H=%lld)", T, H));
+    if (T == 0 || H == 0) return ok();
+    if (T * H > kMaxDim) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "T*H must be below 2^31");
+    I8GS_TRY(check_ptr(kv, "kv"));
+    I8GS_TRY(check_ptr(codes, "codes"));
+    I8GS_TRY(check_ptr(scales, "scales"));
+    I8GS_TRY(check_ld(ld, 128 * H, "ld"));
+    if (T * ld > (int64_t(1) << 40)) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "kv too large");
+    I8GS_TRY(check_device());
+    I8GS_TRY(hip_check(launch_kv_quant((const uint16_t *)kv, T, (int)H, ld, codes, scales, (hipStream_t)stream),
+                       "kv_quant_int8_block128 launch"));
+    return ok();
+}
+
+namespace {
+// Shared checks of the attention products: sizes, heads, grid limits.
+int check_attn(int64_t Mq, int64_t T, int64_t Hq, int64_t Hkv) {
+    if (Mq < 0 || T < 0 || Hq < 0 || Hkv < 0 || Mq > kMaxDim || T > kMaxDim || Hq > kMaxDim || Hkv > kMaxDim)
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE,
+                    fmt("sizes must be in [0, 2^31) (Mq=%lld T=%lld Hq=%lld Hkv=%lld)", Mq, T, Hq, Hkv));
+    if (Hkv == 0 || Hq % Hkv != 0)
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("Hq=%lld must be a multiple of Hkv=%lld > 0", Hq, Hkv));
+    if (Hq > 65535) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "Hq must be at most 65535");
+    if (Mq > 16 * 65535) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "Mq must be at most 1048560");
+    if (Hq * Mq * T > (int64_t(1) << 40)) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "Hq*Mq*T too large");
+    return I8GS_OK;
+}
+}  // namespace
+
+int attn_qk_int8(const int8_t *qq, const float *qs, const int8_t *kq, const float *ks, float scale, int64_t Mq,
+                 int64_t T, int64_t Hq, int64_t Hkv, float *s, int32_t *dots, void *stream) {
+    I8GS_TRY(check_attn(Mq, T, Hq, Hkv));
+    if (!std::isfinite(scale)) return fail(I8GS_ERR_INVALID_ARG, "scale must be finite");
+    if (Mq == 0 || T == 0 || Hq == 0) return ok();
+    I8GS_TRY(check_ptr(qq, "qq"));
+    I8GS_TRY(check_ptr(qs, "qs"));
+    I8GS_TRY(check_ptr(kq, "kq"));
+    I8GS_TRY(check_ptr(ks, "ks"));
+    I8GS_TRY(check_ptr(s, "s"));
+    if (dots) I8GS_TRY(check_ptr(dots, "dots"));
+    I8GS_TRY(check_device());
+    I8GS_TRY(hip_check(launch_attn_qk(qq, qs, kq, ks, scale, (int)Mq, (int)T, (int)Hq, (int)Hkv, s, dots,
+                                      (hipStream_t)stream),
+                       "attn_qk_int8 launch"));
+    return ok();
+}
+
+int attn_pv_int8(const float *p, const int8_t *vq, const float *vs, int64_t Mq, int64_t T, int64_t Hq, int64_t Hkv,
+                 float *out, int8_t *pq, float *ps, void *stream) {
+    I8GS_TRY(check_attn(Mq, T, Hq, Hkv));
+    if (Mq == 0 || Hq == 0) return ok();
+    if (T > 0) {
+        I8GS_TRY(check_ptr(p, "p"));
+        I8GS_TRY(check_ptr(vq, "vq"));
+        I8GS_TRY(check_ptr(vs, "vs"));
+    }
+    I8GS_TRY(check_ptr(out, "out"));
+    if (pq) I8GS_TRY(check_ptr(pq, "pq"));
+    if (ps) I8GS_TRY(check_ptr(ps, "ps"));
+    I8GS_TRY(check_device());
+    I8GS_TRY(hip_check(launch_attn_pv(p, vq, vs, (int)Mq, (int)T, (int)Hq, (int)Hkv, out, pq, ps,
+                                      (hipStream_t)stream),
+                       "attn_pv_int8 launch"));
     return ok();
 }
 

@@ -32,6 +32,12 @@ hipError_t launch_quant_act(const uint16_t *x, int64_t ldx, int M, int K, int8_t
 hipError_t launch_rmsnorm_quant(const uint16_t *x, int64_t ldx, const uint16_t *gamma, double eps, int M, int K,
                                 uint16_t *h, int8_t *qa, float *a_scale, hipStream_t s);
 int rmsnorm_quant_max_k(int64_t M);
+hipError_t launch_kv_quant(const uint16_t *kv, int64_t T, int H, int64_t ld, int8_t *codes, float *scales,
+                           hipStream_t s);
+hipError_t launch_attn_qk(const int8_t *qq, const float *qs, const int8_t *kq, const float *ks, float scale, int Mq,
+                          int T, int Hq, int Hkv, float *s_out, int32_t *dots, hipStream_t s);
+hipError_t launch_attn_pv(const float *p, const int8_t *vq, const float *vs, int Mq, int T, int Hq, int Hkv,
+                          float *out, int8_t *pq_out, float *ps_out, hipStream_t s);
 hipError_t launch_gptq_unpack(const int32_t *qw, const float *ws, int bits, int K, int N,
                               int8_t *q_out, float *w_out, hipStream_t s);
 hipError_t launch_gptq_rtn(const float *w, int bits, int group, int K, int N, int32_t *qw, float *ws,

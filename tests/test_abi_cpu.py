@@ -222,3 +222,27 @@ def test_rmsnorm_quant_validation(lib):
     assert f(A, 40000, A, 1e-6, 4, 40000, NUL, A, A, NUL) == 2     # K past the register limit
     assert "registers" in lib.i8gs_last_error().decode()
     assert f(A, 512, A, 1e-6, 0, 512, NUL, A, A, NUL) == 0
+
+
+def test_kv_codec_and_attention_validation(lib):
+    kvq = lib.kv_quant_int8_block128
+    assert kvq(A, 100, 4, 1, A, A, NUL) == 2        # ld < 128*H
+    assert kvq(A, 256, 4, 2, MIS, A, NUL) == 3      # codes misaligned
+    assert kvq(NUL, 256, 4, 2, A, A, NUL) == 1      # kv NULL
+    assert kvq(A, 256, 0, 2, A, A, NUL) == 0        # empty: no-op
+    assert kvq(A, 256, -1, 2, A, A, NUL) == 2
+    qk = lib.attn_qk_int8
+    assert qk(A, A, A, A, 0.088, 4, 16, 6, 4, A, NUL, NUL) == 2      # Hq % Hkv
+    assert "multiple" in lib.i8gs_last_error().decode()
+    assert qk(A, A, A, A, 0.088, 4, 16, 8, 0, A, NUL, NUL) == 2      # Hkv == 0
+    assert qk(A, A, A, A, float("inf"), 4, 16, 8, 4, A, NUL, NUL) == 1
+    assert qk(A, A, A, A, 0.088, 4, 16, 70000, 2, A, NUL, NUL) == 2  # grid limit on heads
+    assert qk(A, A, A, A, 0.088, 4, 16, 8, 4, A, MIS, NUL) == 3      # dots misaligned
+    assert qk(A, NUL, A, A, 0.088, 4, 16, 8, 4, A, NUL, NUL) == 1    # qs NULL
+    assert qk(NUL, NUL, NUL, NUL, 0.088, 4, 0, 8, 4, NUL, NUL, NUL) == 0  # T == 0: no-op
+    pv = lib.attn_pv_int8
+    assert pv(A, A, A, 4, 16, 6, 4, A, NUL, NUL, NUL) == 2
+    assert pv(A, A, A, 4, 16, 8, 4, A, NUL, MIS, NUL) == 3           # ps misaligned
+    assert pv(A, NUL, A, 4, 16, 8, 4, A, NUL, NUL, NUL) == 1         # vq NULL
+    assert pv(NUL, NUL, NUL, 0, 16, 8, 4, NUL, NUL, NUL, NUL) == 0   # Mq == 0: no-op
+    assert pv(A, A, A, 4, 16, 8, 4, NUL, NUL, NUL, NUL) == 1         # out NULL
