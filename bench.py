@@ -480,6 +480,40 @@ def main():
                                 "note": "one launch per layer input in place of a normalisation kernel "
                                         "followed by the quantisation kernel"}
 
+    if not args.no_extras:
+        # ---------------- INT8 block-g128 KV cache: codec, QK and PV for one block of 8 draft
+        # queries (32 query heads over 8 KV heads) against a 2048-token window and a 32768-token
+        # context; inputs cycle through cold copies
+        kv = {}
+        Hq, Hkv, Mq = 32, 8, 8
+        for T in (2048, 32768):
+            kb = torch.from_numpy(synth.activations_bf16(0, f"bench-k{T}", T * Hkv, 128, True).view(np.int16)) \
+                .view(torch.bfloat16).reshape(T, Hkv, 128).to(dev)
+            qb = torch.from_numpy(synth.activations_bf16(0, f"bench-q{T}", Mq * Hq, 128, True).view(np.int16)) \
+                .view(torch.bfloat16).reshape(Mq, Hq, 128).to(dev)
+            kq, ks = i8.kv_quant_int8_block128(kb)
+            qq, qs = i8.kv_quant_int8_block128(qb)
+            codes_b = T * Hkv * (256 + 128 + 4)
+            us_c = timed(("kvq", T), [lambda c=c: i8.kv_quant_int8_block128(c[0], codes=kq, scales=ks)
+                                      for c in cold_copies((kb,), codes_b)], 50)
+            sc = torch.empty((Hq, Mq, T), dtype=torch.float32, device=dev)
+            qk_b = Mq * Hq * 132 + T * Hkv * 132 + Hq * Mq * T * 4
+            us_qk = timed(("qk", T), [lambda c=c: i8.attn_qk_int8(qq, qs, c[0], c[1], 128 ** -0.5, s=sc)
+                                      for c in cold_copies((kq, ks), qk_b)], 50)
+            p = torch.softmax(sc, dim=2)
+            o = torch.empty((Hq, Mq, 128), dtype=torch.float32, device=dev)
+            pv_b = Hq * Mq * T * 4 + T * Hkv * 132 + Hq * Mq * 128 * 4
+            us_pv = timed(("pv", T), [lambda c=c: i8.attn_pv_int8(c[0], c[1], c[2], out=o)
+                                      for c in cold_copies((p, kq, ks), pv_b)], 50)
+            for name, us, b in (("codec", us_c, codes_b), ("qk", us_qk, qk_b), ("pv", us_pv, pv_b)):
+                kv[f"{name}_T{T}"] = {"us": round(us, 3), "bytes": b, "GBps": round(b / (us * 1e-6) / 1e9, 1),
+                                      "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            del kb, qb, kq, ks, qq, qs, sc, p, o
+            torch.cuda.empty_cache()
+        kv["shape"] = {"Mq": Mq, "Hq": Hq, "Hkv": Hkv, "head_dim": 128}
+        out["kv_int8"] = kv
+        log("kv int8: " + ", ".join(f"{k} {v['us']:.1f} us" for k, v in kv.items() if "us" in v))
+
     if not args.no_lm_head:
         # ---------------- vocabulary heads: 248320 columns (naturally cold: 0.64-1.27 GB of codes)
         L = synth.LAYERS["lm_head"]

@@ -317,8 +317,8 @@ int kv_quant_int8_block128(const void *kv, int64_t ld, int64_t T, int64_t H, int
  *   kq int8 [T, Hkv, 128], ks fp32 [T, Hkv] (the K cache)
  *   scale   finite fp32 (e.g. 1/sqrt(128))
  *   s       fp32 [Hq, Mq, T], output;  dots  int32 [Hq, Mq, T] or NULL, output
- * Hq % Hkv == 0, Hkv > 0, Hq <= 65535, Mq <= 1048560, Hq*Mq*T <= 2^40.  Empty sizes
- * are a no-op.
+ * Hq % Hkv == 0, Hkv > 0, Hq <= 65535, (Hq/Hkv)*Mq <= 2097120, Hq*Mq*T <= 2^40.
+ * Empty sizes are a no-op.
  */
 int attn_qk_int8(const int8_t *qq, const float *qs, const int8_t *kq, const float *ks, float scale, int64_t Mq,
                  int64_t T, int64_t Hq, int64_t Hkv, float *s, int32_t *dots, void *stream);
@@ -333,17 +333,25 @@ int attn_qk_int8(const int8_t *qq, const float *qs, const int8_t *kq, const floa
  *   ps[h,i,b]  = max_{t in block b} |p'| / 127  (fp32; a last partial block takes its tokens)
  *   pq[h,i,t]  = clamp(rint(p' / ps), -127, 127)  (0 where ps = 0; IEEE division)
  *   out[h,i,d] = sum_b ps[h,i,b] * sum_{t in b} pq[h,i,t] * vq[t, hk, d]
- * The block sums are exact int32; the fold over blocks is fp32, so out is within
- * (B + 2) * 2^-24 * sum_b |ps| * sum_t |pq * vq| of the exact value (B = ceil(T/128)).
- * pq and ps are bit-exact.
+ * The block sums are exact int32; the fold over blocks is fp32 (split over token ranges
+ * when there are few rows, the ranges summed in a fixed order), so out is within
+ * (B + 2) * 2^-24 * sum_b |ps| * sum_t |pq * vq| of the exact value (B = ceil(T/128))
+ * and the same inputs always give the same bits.  pq and ps are bit-exact.
  *   p   fp32 [Hq, Mq, T] (e.g. softmax of the QK scores);  vq int8 [T, Hkv, 128],
  *   vs  fp32 [T, Hkv] (the V cache)
  *   out fp32 [Hq, Mq, 128], output (zeros when T == 0)
  *   pq  int8 [Hq, Mq, T] or NULL;  ps  fp32 [Hq, Mq, B] or NULL (outputs)
+ *   workspace  attn_pv_int8_workspace_bytes(Mq, T, Hq, Hkv) bytes (NULL if 0): the
+ *              fp32 sums of the token ranges, written and read within the call (no
+ *              initial contents needed; not shared with a concurrent call)
  * Size limits as for attn_qk_int8.
  */
 int attn_pv_int8(const float *p, const int8_t *vq, const float *vs, int64_t Mq, int64_t T, int64_t Hq, int64_t Hkv,
-                 float *out, int8_t *pq, float *ps, void *stream);
+                 float *out, int8_t *pq, float *ps, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes attn_pv_int8 needs for these sizes (0: none), or (size_t)-1 for
+ * invalid sizes. */
+size_t attn_pv_int8_workspace_bytes(int64_t Mq, int64_t T, int64_t Hq, int64_t Hkv);
 
 #ifdef __cplusplus
 }

@@ -41,7 +41,7 @@ EXPORTS = (
     "gemm_w8a8_g128_group_partials", "gemm_w8a8_g128_group_partials_ex", "gemm_w4a16_g128", "gptq_unpack",
     "gptq_quantize_rtn", "gemm_w8a8_g128_noalloc", "i8gs_noalloc_scratch_bytes", "gemm_weight_only",
     "gptq_quantize_rtn_group", "rmsnorm_quant_per_token", "kv_quant_int8_block128", "attn_qk_int8",
-    "attn_pv_int8",
+    "attn_pv_int8", "attn_pv_int8_workspace_bytes",
 )
 
 _lib = None
@@ -90,7 +90,9 @@ def load_library(path: str = LIB_PATH):
     lib.i8gs_noalloc_scratch_bytes.restype = S
     lib.kv_quant_int8_block128.argtypes = [P, I64, I64, I64, P, P, P]
     lib.attn_qk_int8.argtypes = [P, P, P, P, ctypes.c_float, I64, I64, I64, I64, P, P, P]
-    lib.attn_pv_int8.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, P]
+    lib.attn_pv_int8.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, P, S, P]
+    lib.attn_pv_int8_workspace_bytes.argtypes = [I64, I64, I64, I64]
+    lib.attn_pv_int8_workspace_bytes.restype = S
     lib.gptq_unpack.argtypes = [P, P, I, I64, I64, P, P, P]
     lib.gptq_quantize_rtn.argtypes = [P, I, I64, I64, P, P, P]
     for name in ("quant_act_per_token", "gemm_w8a8_g128", "gemm_w8a8_g128_ex", "gemm_w8a8_g128_group_partials",
@@ -453,6 +455,10 @@ def attn_pv_int8(p: torch.Tensor, vq: torch.Tensor, vs: torch.Tensor, want_codes
     B = (T + 127) // 128
     pq = torch.empty((Hq, Mq, T), dtype=torch.int8, device=p.device) if want_codes else None
     ps = torch.empty((Hq, Mq, B), dtype=torch.float32, device=p.device) if want_codes else None
+    nbytes = load_library().attn_pv_int8_workspace_bytes(Mq, T, Hq, Hkv)
+    if nbytes == ctypes.c_size_t(-1).value:
+        raise ValueError(f"invalid attention sizes Mq={Mq} T={T} Hq={Hq} Hkv={Hkv}")
+    ws = _workspace(p.device, int(nbytes))
     _raise(load_library().attn_pv_int8(_ptr(p), _ptr(vq), _ptr(vs), Mq, T, Hq, Hkv, _ptr(out), _ptr(pq), _ptr(ps),
-                                       _stream(p.device)))
+                                       _ptr(ws), int(nbytes), _stream(p.device)))
     return out, pq, ps

@@ -447,7 +447,9 @@ int check_attn(int64_t Mq, int64_t T, int64_t Hq, int64_t Hkv) {
     if (Hkv == 0 || Hq % Hkv != 0)
         return fail(I8GS_ERR_UNSUPPORTED_SHAPE, fmt("Hq=%lld must be a multiple of Hkv=%lld > 0", Hq, Hkv));
     if (Hq > 65535) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "Hq must be at most 65535");
-    if (Mq > 16 * 65535) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "Mq must be at most 1048560");
+    // rows of one KV head group, (Hq/Hkv) * Mq: 32 per workgroup of the PV kernel's grid
+    if (Hkv > 0 && Hq / Hkv * Mq > 32 * 65535)
+        return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "(Hq/Hkv)*Mq must be at most 2097120");
     if (Hq * Mq * T > (int64_t(1) << 40)) return fail(I8GS_ERR_UNSUPPORTED_SHAPE, "Hq*Mq*T too large");
     return I8GS_OK;
 }
@@ -471,8 +473,16 @@ int attn_qk_int8(const int8_t *qq, const float *qs, const int8_t *kq, const floa
     return ok();
 }
 
+size_t attn_pv_int8_workspace_bytes(int64_t Mq, int64_t T, int64_t Hq, int64_t Hkv) {
+    if (Mq < 0 || T < 0 || Hq < 0 || Hkv <= 0 || Mq > kMaxDim || T > kMaxDim || Hq > kMaxDim || Hq % Hkv != 0)
+        return (size_t)-1;
+    if (Mq == 0 || Hq == 0) return 0;
+    const PvPlan pl = attn_pv_plan(Mq, T, Hq, Hkv);
+    return pl.part_bytes;
+}
+
 int attn_pv_int8(const float *p, const int8_t *vq, const float *vs, int64_t Mq, int64_t T, int64_t Hq, int64_t Hkv,
-                 float *out, int8_t *pq, float *ps, void *stream) {
+                 float *out, int8_t *pq, float *ps, void *workspace, size_t workspace_bytes, void *stream) {
     I8GS_TRY(check_attn(Mq, T, Hq, Hkv));
     if (Mq == 0 || Hq == 0) return ok();
     if (T > 0) {
@@ -483,9 +493,17 @@ int attn_pv_int8(const float *p, const int8_t *vq, const float *vs, int64_t Mq, 
     I8GS_TRY(check_ptr(out, "out"));
     if (pq) I8GS_TRY(check_ptr(pq, "pq"));
     if (ps) I8GS_TRY(check_ptr(ps, "ps"));
+    const PvPlan pl = attn_pv_plan(Mq, T, Hq, Hkv);
+    const size_t need = pl.part_bytes;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(I8GS_ERR_WORKSPACE, fmt("workspace of %lld bytes needed, %lld given", (long long)need,
+                                                 workspace ? (long long)workspace_bytes : 0LL));
+        if (!aligned16(workspace)) return fail(I8GS_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    }
     I8GS_TRY(check_device());
     I8GS_TRY(hip_check(launch_attn_pv(p, vq, vs, (int)Mq, (int)T, (int)Hq, (int)Hkv, out, pq, ps,
-                                      (hipStream_t)stream),
+                                      need ? (float *)workspace : nullptr, (hipStream_t)stream),
                        "attn_pv_int8 launch"));
     return ok();
 }

@@ -36,8 +36,16 @@ hipError_t launch_kv_quant(const uint16_t *kv, int64_t T, int H, int64_t ld, int
                            hipStream_t s);
 hipError_t launch_attn_qk(const int8_t *qq, const float *qs, const int8_t *kq, const float *ks, float scale, int Mq,
                           int T, int Hq, int Hkv, float *s_out, int32_t *dots, hipStream_t s);
+// PV launch plan: S splits of the token blocks (blocks_per_split each), `tiles` row
+// tiles of 32 rows; part_bytes of fp32 partial sums when S > 1.
+struct PvPlan {
+    int S, blocks_per_split;
+    int64_t tiles;
+    size_t part_bytes;
+};
+PvPlan attn_pv_plan(int64_t Mq, int64_t T, int64_t Hq, int64_t Hkv);
 hipError_t launch_attn_pv(const float *p, const int8_t *vq, const float *vs, int Mq, int T, int Hq, int Hkv,
-                          float *out, int8_t *pq_out, float *ps_out, hipStream_t s);
+                          float *out, int8_t *pq_out, float *ps_out, float *part, hipStream_t s);
 hipError_t launch_gptq_unpack(const int32_t *qw, const float *ws, int bits, int K, int N,
                               int8_t *q_out, float *w_out, hipStream_t s);
 hipError_t launch_gptq_rtn(const float *w, int bits, int group, int K, int N, int32_t *qw, float *ws,

@@ -237,12 +237,22 @@ def test_kv_codec_and_attention_validation(lib):
     assert qk(A, A, A, A, 0.088, 4, 16, 8, 0, A, NUL, NUL) == 2      # Hkv == 0
     assert qk(A, A, A, A, float("inf"), 4, 16, 8, 4, A, NUL, NUL) == 1
     assert qk(A, A, A, A, 0.088, 4, 16, 70000, 2, A, NUL, NUL) == 2  # grid limit on heads
+    assert qk(A, A, A, A, 0.088, 1048560, 1, 64, 1, A, NUL, NUL) == 2  # rows per KV head group
     assert qk(A, A, A, A, 0.088, 4, 16, 8, 4, A, MIS, NUL) == 3      # dots misaligned
     assert qk(A, NUL, A, A, 0.088, 4, 16, 8, 4, A, NUL, NUL) == 1    # qs NULL
     assert qk(NUL, NUL, NUL, NUL, 0.088, 4, 0, 8, 4, NUL, NUL, NUL) == 0  # T == 0: no-op
     pv = lib.attn_pv_int8
-    assert pv(A, A, A, 4, 16, 6, 4, A, NUL, NUL, NUL) == 2
-    assert pv(A, A, A, 4, 16, 8, 4, A, NUL, MIS, NUL) == 3           # ps misaligned
-    assert pv(A, NUL, A, 4, 16, 8, 4, A, NUL, NUL, NUL) == 1         # vq NULL
-    assert pv(NUL, NUL, NUL, 0, 16, 8, 4, NUL, NUL, NUL, NUL) == 0   # Mq == 0: no-op
-    assert pv(A, A, A, 4, 16, 8, 4, NUL, NUL, NUL, NUL) == 1         # out NULL
+    W = lib.attn_pv_int8_workspace_bytes
+    assert W(8, 32768, 32, 8) > 0                                    # decode: the token blocks are split
+    assert W(4096, 4096, 32, 8) == 0                                 # enough row tiles: no split
+    assert W(8, 0, 32, 8) == 0 and W(0, 100, 32, 8) == 0
+    assert W(8, 100, 6, 4) == ctypes.c_size_t(-1).value
+    need = W(8, 32768, 32, 8)
+    assert pv(A, A, A, 4, 16, 6, 4, A, NUL, NUL, NUL, 0, NUL) == 2
+    assert pv(A, A, A, 4, 16, 8, 4, A, NUL, MIS, NUL, 0, NUL) == 3           # ps misaligned
+    assert pv(A, NUL, A, 4, 16, 8, 4, A, NUL, NUL, NUL, 0, NUL) == 1         # vq NULL
+    assert pv(NUL, NUL, NUL, 0, 16, 8, 4, NUL, NUL, NUL, NUL, 0, NUL) == 0   # Mq == 0: no-op
+    assert pv(A, A, A, 4, 16, 8, 4, NUL, NUL, NUL, NUL, 0, NUL) == 1         # out NULL
+    assert pv(A, A, A, 8, 32768, 32, 8, A, NUL, NUL, NUL, 0, NUL) == 4       # workspace missing
+    assert pv(A, A, A, 8, 32768, 32, 8, A, NUL, NUL, A, need - 1, NUL) == 4  # workspace too small
+    assert pv(A, A, A, 8, 32768, 32, 8, A, NUL, NUL, MIS, need, NUL) == 3    # workspace misaligned

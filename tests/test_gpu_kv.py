@@ -114,11 +114,30 @@ def _pv_check(p, vq, vs, what):
 
 
 @pytest.mark.parametrize("Mq,T,Hq,Hkv", [(8, 2048, 32, 8), (3, 77, 4, 1), (17, 129, 2, 2), (1, 1, 1, 1),
-                                         (20, 300, 8, 4), (8, 16384, 32, 8)])
+                                         (20, 300, 8, 4), (8, 16384, 32, 8), (8, 5000, 32, 8), (2, 1000, 4, 4),
+                                         (512, 700, 32, 8)])
 def test_attn_pv_int8(Mq, T, Hq, Hkv):
     p = _probs(5, f"p{Mq}x{T}", Hq, Mq, T)
     vq, vs = oracle.kv_quant_block128(_kv(5, f"v{T}", T, Hkv))
     _pv_check(p, vq, vs, f"{Mq}x{T}x{Hq}/{Hkv}")
+
+
+def test_attn_pv_split_is_deterministic():
+    """With the token blocks split over workgroups (few rows, long context) the split sums
+    are added in a fixed order: repeated calls give the same bits, also with a call of
+    another shape on the same workspace in between."""
+    Mq, T, Hq, Hkv = 8, 9000, 32, 8
+    assert i8.load_library().attn_pv_int8_workspace_bytes(Mq, T, Hq, Hkv) > 0
+    p = dev(_probs(8, "pdet", Hq, Mq, T))
+    vq, vs = oracle.kv_quant_block128(_kv(8, "vdet", T, Hkv))
+    vq, vs = dev(vq), dev(vs)
+    a, _, _ = i8.attn_pv_int8(p, vq, vs)
+    small = dev(_probs(8, "pdet2", 4, 3, 300))
+    vq2, vs2 = oracle.kv_quant_block128(_kv(8, "vdet2", 300, 1))
+    i8.attn_pv_int8(small, dev(vq2), dev(vs2))
+    b, _, _ = i8.attn_pv_int8(p, vq, vs)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
 
 
 def test_attn_pv_degenerate_rows():
