@@ -57,7 +57,7 @@ HBM_PEAK_GBS = 8000.0
 # for the kernel sources they were taken with, identified by the SHA-256 of the code in
 # DECODE_SOURCES (comments and whitespace aside); after any change to that code `traffic`
 # is reported as null.
-DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h", "include/i8gs.h")
+DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h")
 DECODE_TRAFFIC = {
     "sources_sha256": "84a9eb0eea502d269f5604bcde36860788df78a2f63b532cdf897a2b3465c55b",
     "fetch": {"qkv": 36814661, "o_proj": 26535249, "gate_up": 192737799, "down": 107581243},
@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="no timing: 4 decode steps plus a 256 MiB device copy (the calibration kernel), for "
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--counter-probe", choices=("prefill", "w4a16"),
+                    help="no timing: two launches of each prefill GEMM (M=4096, five layers) or of each W4A16 "
+                         "GEMM (M=8 and 64, four decode layers), for rocprofv3 --pmc runs")
     return ap.parse_args()
 
 
@@ -245,6 +248,37 @@ def main():
     log(f"inputs ready in {time.time() - t0:.1f}s: {nsets} weight sets of {set_bytes / 1e6:.1f} MB")
 
     timer = Timer(torch)
+
+    if args.counter_probe:
+        # Counter runs on the secondary kernels: two launches per layer and size, in order.
+        del wsets
+        torch.cuda.empty_cache()
+        if args.counter_probe == "prefill":
+            for L in synth.PREFILL_LAYERS:
+                xb = synth.activations_bf16(0, f"bench-prefill-{L.name}", 4096, L.K, outliers=True)
+                x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+                w = torch.from_numpy(synth.weights_f32(0, f"bench-prefill-{L.name}", L.K, L.N)).to(dev)
+                qw, sc = i8.gptq_quantize_rtn(w, 8)
+                qa, s = i8.quant_act_per_token(x)
+                y = torch.empty((4096, L.N), dtype=torch.bfloat16, device=dev)
+                for _ in range(2):
+                    i8.gemm_w8a8_g128(qw, sc, qa=qa, a_scale=s, y=y)
+                torch.cuda.synchronize()
+                del x, w, qw, sc, qa, s, y
+        else:
+            for L in layers:
+                w = torch.from_numpy(synth.weights_f32(0, f"bench-w4-{L.name}", L.K, L.N)).to(dev)
+                qw, sc = i8.gptq_quantize_rtn(w, 4)
+                for Mw in (8, 64):
+                    xb = synth.activations_bf16(0, f"bench-w4-{L.name}-{Mw}", Mw, L.K, outliers=True)
+                    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+                    y = torch.empty((Mw, L.N), dtype=torch.bfloat16, device=dev)
+                    for _ in range(2):
+                        i8.gemm_w4a16_g128(x, qw, sc, y)
+                torch.cuda.synchronize()
+                del w, qw, sc
+        print(json.dumps({"counter_probe": args.counter_probe}), flush=True)
+        return
 
     if args.traffic_probe:
         # Counter runs: a plain copy of known size first (its FETCH_SIZE / WRITE_SIZE give

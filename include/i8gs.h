@@ -341,9 +341,11 @@ int attn_qk_int8(const int8_t *qq, const float *qs, const int8_t *kq, const floa
  *   vs  fp32 [T, Hkv] (the V cache)
  *   out fp32 [Hq, Mq, 128], output (zeros when T == 0)
  *   pq  int8 [Hq, Mq, T] or NULL;  ps  fp32 [Hq, Mq, B] or NULL (outputs)
- *   workspace  attn_pv_int8_workspace_bytes(Mq, T, Hq, Hkv) bytes (NULL if 0): the
- *              fp32 sums of the token ranges, written and read within the call (no
- *              initial contents needed; not shared with a concurrent call)
+ *   workspace  attn_pv_int8_workspace_bytes(Mq, T, Hq, Hkv) bytes (NULL if 0), laid
+ *              out as for the GEMMs: the 64 KiB counter region first (not touched
+ *              here, so one workspace serves both), then the fp32 sums of the token
+ *              ranges, written and read within the call; not shared with a
+ *              concurrent call
  * Size limits as for attn_qk_int8.
  */
 int attn_pv_int8(const float *p, const int8_t *vq, const float *vs, int64_t Mq, int64_t T, int64_t Hq, int64_t Hkv,

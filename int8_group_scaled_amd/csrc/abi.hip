@@ -478,7 +478,7 @@ size_t attn_pv_int8_workspace_bytes(int64_t Mq, int64_t T, int64_t Hq, int64_t H
         return (size_t)-1;
     if (Mq == 0 || Hq == 0) return 0;
     const PvPlan pl = attn_pv_plan(Mq, T, Hq, Hkv);
-    return pl.part_bytes;
+    return pl.part_bytes ? kCounterBytes + pl.part_bytes : 0;
 }
 
 int attn_pv_int8(const float *p, const int8_t *vq, const float *vs, int64_t Mq, int64_t T, int64_t Hq, int64_t Hkv,
@@ -494,7 +494,8 @@ int attn_pv_int8(const float *p, const int8_t *vq, const float *vs, int64_t Mq, 
     if (pq) I8GS_TRY(check_ptr(pq, "pq"));
     if (ps) I8GS_TRY(check_ptr(ps, "ps"));
     const PvPlan pl = attn_pv_plan(Mq, T, Hq, Hkv);
-    const size_t need = pl.part_bytes;
+    // the common workspace layout: the (here unused) counter region first, left as it is
+    const size_t need = pl.part_bytes ? kCounterBytes + pl.part_bytes : 0;
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(I8GS_ERR_WORKSPACE, fmt("workspace of %lld bytes needed, %lld given", (long long)need,
@@ -503,7 +504,8 @@ int attn_pv_int8(const float *p, const int8_t *vq, const float *vs, int64_t Mq, 
     }
     I8GS_TRY(check_device());
     I8GS_TRY(hip_check(launch_attn_pv(p, vq, vs, (int)Mq, (int)T, (int)Hq, (int)Hkv, out, pq, ps,
-                                      need ? (float *)workspace : nullptr, (hipStream_t)stream),
+                                      need ? (float *)((char *)workspace + kCounterBytes) : nullptr,
+                                      (hipStream_t)stream),
                        "attn_pv_int8 launch"));
     return ok();
 }

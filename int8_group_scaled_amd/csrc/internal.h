@@ -73,6 +73,10 @@ size_t w8a8_gemm_workspace(int M, int N, int K, int kernel, int workgroups);
 bool decode_y_fits(int64_t M, int64_t ldy);
 bool prefill_y_fits(int64_t M, int64_t ldy);
 hipError_t launch_w8a8_gemm(const W8A8Args &a, hipStream_t s);
+// The 256 x 256-tile prefill kernel (y, or the group partials when a.P is set) and the
+// split-K pieces its plan needs.
+hipError_t launch_prefill(const W8A8Args &a, hipStream_t s);
+size_t prefill_gemm_workspace(int M, int N, int K);
 
 // A validated W8A8 call: what it needs and which kernel family it takes.
 struct W8A8Plan {

@@ -140,6 +140,24 @@ def test_attn_pv_split_is_deterministic():
     assert torch.equal(a, b)
 
 
+def test_attn_pv_leaves_the_gemm_counters_alone():
+    """PV and the split-K GEMMs share the binding's workspace: the GEMM's arrival counters
+    at its start stay zero across a split PV call, so a split-K GEMM after it is unchanged."""
+    from parity import rtn_weights
+    K, N, M = 5120, 6144, 8
+    xb = synth.activations_bf16(9, "pv-ws-x", M, K, True)
+    qw, ws = rtn_weights(9, "pv-ws", K, N, 4)
+    x, qw, ws = dev_bf16(xb), dev(qw), dev(ws)
+    y1 = i8.gemm_w4a16_g128(x, qw, ws)
+    Mq, T, Hq, Hkv = 8, 9000, 32, 8
+    p = dev(_probs(9, "pv-ws-p", Hq, Mq, T))
+    vq, vs = oracle.kv_quant_block128(_kv(9, "pv-ws-v", T, Hkv))
+    i8.attn_pv_int8(p, dev(vq), dev(vs))
+    y2 = i8.gemm_w4a16_g128(x, qw, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
 def test_attn_pv_degenerate_rows():
     """A query row of zero probabilities (every block scale 0, output 0), a one-hot row
     (the output is that token's V row times its scale, up to the codec), and a row whose
