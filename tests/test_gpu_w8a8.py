@@ -321,3 +321,35 @@ def test_large_row_stride_y(M, K, N, ldy):
     assert_within_tolerance(host_bf16_bits(y.contiguous()), y_exact, T, K, what=f"ldy={ldy} {M}x{K}x{N}")
     del ybuf
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("layer", ["qkv", "down"])
+def test_graph_replays_match_eager(layer):
+    """The decode linear from bf16 x (quantisation into the workspace, then the K-split
+    GEMM whose arrival counters must return to zero) captured as a HIP graph: three
+    replays, with eager calls of another shape and host synchronisations between them,
+    each give the eager result bit for bit."""
+    L = synth.LAYERS[layer]
+    M = 64
+    xb = synth.activations_bf16(3, f"graph-{layer}", M, L.K, True)
+    qw, ws = rtn_weights(3, f"graph-{layer}", L.K, L.N, 8)
+    x, qw, ws = dev_bf16(xb), dev(qw), dev(ws)
+    y_eager = i8.gemm_w8a8_g128(qw, ws, x=x)
+    other = synth.LAYERS["o_proj"]
+    xo = dev_bf16(synth.activations_bf16(3, "graph-other", 8, other.K, True))
+    qwo, wso = (dev(a) for a in rtn_weights(3, "graph-other", other.K, other.N, 8))
+    cap = torch.cuda.Stream()
+    y = torch.empty_like(y_eager)
+    with torch.cuda.stream(cap):
+        i8.gemm_w8a8_g128(qw, ws, x=x, y=y)  # the binding's workspace for this stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        i8.gemm_w8a8_g128(qw, ws, x=x, y=y)
+    for r in range(3):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {r}"
+        i8.gemm_w8a8_g128(qwo, wso, x=xo)
+        torch.cuda.synchronize()
