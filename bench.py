@@ -59,9 +59,9 @@ HBM_PEAK_GBS = 8000.0
 # is reported as null.
 DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h")
 DECODE_TRAFFIC = {
-    "sources_sha256": "84a9eb0eea502d269f5604bcde36860788df78a2f63b532cdf897a2b3465c55b",
-    "fetch": {"qkv": 36814661, "o_proj": 26535249, "gate_up": 192737799, "down": 107581243},
-    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456544, "down": 8528640},
+    "sources_sha256": "f72b723771a8b93769b6ae71bafdda6e0d5a9e3aec764757f6fbba467268f946",
+    "fetch": {"qkv": 36823840, "o_proj": 26537984, "gate_up": 192127328, "down": 107585504},
+    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456456, "down": 8528640},
 }
 EVENT_EVERY = 8  # per-kernel HIP events on every 8th timed step (each event adds a gap)
 INT8_PEAK_TOPS = 5000.0
@@ -341,7 +341,23 @@ def main():
                              "quant_us": round(qm, 3), "gemm_GBps": round(b / (gm * 1e-6) / 1e9, 1),
                              "gemm_frac_hbm": round(b / (gm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     achieved = g_bytes / (g_us * 1e-6) / 1e9
-    log(f"decode step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s; GEMM kernels {achieved:.0f} GB/s")
+    # Cross-check without an event around every launch: per layer, 32 back-to-back GEMM
+    # launches (weight sets rotated, so still read from HBM) between two events.  The
+    # difference to gemm_us is the dispatch time an event pair brackets.
+    for li, L in enumerate(layers):
+        torch.cuda.synchronize()
+        spin(torch, 2)
+        e0 = timer.mark()
+        for r in range(32):
+            qw, sc = wsets[r % nsets][li]
+            i8.gemm_w8a8_g128(qw, sc, qa=qas[li], a_scale=scs[li], y=ys[li])
+        e1 = timer.mark()
+        timer.add(("b2b", L.name), e0, e1)
+        torch.cuda.synchronize()
+        per_layer[L.name]["gemm_us_back_to_back"] = round(timer.mean_us(("b2b", L.name))[0] / 32, 3)
+    log(f"decode step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s; GEMM kernels {achieved:.0f} GB/s "
+        f"(back to back: " + ", ".join(f"{L.name} {per_layer[L.name]['gemm_us_back_to_back']:.1f}" for L in layers)
+        + " us)")
     traffic = None
     if decode_sources_sha256() == DECODE_TRAFFIC["sources_sha256"]:
         traffic = round(sum(DECODE_TRAFFIC["fetch"][L.name] + DECODE_TRAFFIC["write"][L.name] for L in layers)
