@@ -8,7 +8,7 @@
 // codes = clamp(rint(x / scale), -127, 127).
 //
 // QK: s[h, i, t] = scale * qs[i, h] * ks[t, hk] * sum_d qq[i, h, d] * kq[t, hk, d], with
-// hk = h / (Hq / Hkv); the dot is exact in int32 (v_mfma_i32_16x16x64_i8, two per 16x16
+// hk = h / (Hq / Hkv); the dot is exact in int32 (v_mfma_i32_32x32x32_i8, four per 32x32
 // tile of queries x tokens), the three scale products are fp32.
 //
 // PV (INT8 PV): for probabilities p [Hq, Mq, T] and the INT8 V cache, the V scale of
@@ -57,43 +57,57 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t *__restric
 // form R = (Hq/Hkv) * Mq rows r = (h - hk*Hq/Hkv) * Mq + i; row r is row hk*R + r of
 // the [Hq*Mq, ...] score, probability and output matrices.
 
-// QK: a workgroup covers 64 tokens (16 per wave) and up to 64 rows of one group (four
-// 16-row tiles).  A wave loads its tokens' K vectors once (the B operand: lane li = token,
-// 16 bytes of the head dimension at 16*kb + 64*step) and multiplies them with each row
-// tile's query vectors (the A operand, the same byte placement) on 16x16x64 MFMA.
+// QK: a workgroup covers 128 tokens (32 per wave) and up to 64 rows of one group (two
+// 32-row tiles).  A wave loads its tokens' K vectors once as the B operand of
+// v_mfma_i32_32x32x32_i8 (lane l: token l % 32, 16 bytes of the head dimension at
+// 16*(l/32) + 32*step, four steps) and multiplies them with each row tile's query
+// vectors (the A operand, the same byte placement).  Register i of the result holds
+// token l % 32 of row 8*(i/4) + 4*(l/32) + i%4, so each store instruction writes two
+// rows of 32 consecutive scores (128 bytes each).
+typedef int v16i_kv __attribute__((ext_vector_type(16)));
+
 __global__ __launch_bounds__(256) void attn_qk_kernel(const int8_t *__restrict__ qq, const float *__restrict__ qs,
                                                       const int8_t *__restrict__ kq, const float *__restrict__ ks,
                                                       float scale, int Mq, int T, int Hq, int Hkv,
                                                       float *__restrict__ s_out, int32_t *__restrict__ dots) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int hk = blockIdx.y, rep = Hq / Hkv, R = rep * Mq;
-    const int t0 = blockIdx.x * 64 + wave * 16;
+    const int t0 = blockIdx.x * 128 + wave * 32;
     if (t0 >= T) return;
-    const int li = lane & 15, kb = lane >> 4;
+    const int li = lane & 31, h = lane >> 5;
     const int kt = min(t0 + li, T - 1);  // tokens past the end: never stored
-    const int8_t *krow = kq + ((int64_t)kt * Hkv + hk) * 128 + 16 * kb;
-    const v4i b0 = *reinterpret_cast<const v4i *>(krow), b1 = *reinterpret_cast<const v4i *>(krow + 64);
+    const int8_t *krow = kq + ((int64_t)kt * Hkv + hk) * 128 + 16 * h;
+    v4i b[4];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 4; ++ks2) b[ks2] = *reinterpret_cast<const v4i *>(krow + 32 * ks2);
     const int t = t0 + li;
     const float kscale = ks[(int64_t)kt * Hkv + hk];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const int r0 = blockIdx.z * 64 + rt * 16;
+    for (int rt = 0; rt < 2; ++rt) {
+        const int r0 = blockIdx.z * 64 + rt * 32;
         if (r0 >= R) break;
+        // lane li's row of the tile: its query vector (A operand) and scale * qs (shared by
+        // shuffles with the lanes that store that row)
         const int ra = min(r0 + li, R - 1);
-        const int8_t *qrow = qq + ((int64_t)(ra % Mq) * Hq + hk * rep + ra / Mq) * 128 + 16 * kb;
-        v4i acc = v4i{0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const v4i *>(qrow), b0, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const v4i *>(qrow + 64), b1, acc, 0, 0, 0);
-        // lane: token t, rows r0 + 4*kb + j
-        if (t < T) {
+        const int qi = ra % Mq, qh = hk * rep + ra / Mq;
+        const int8_t *qrow = qq + ((int64_t)qi * Hq + qh) * 128 + 16 * h;
+        const float sq = scale * qs[(int64_t)qi * Hq + qh];
+        v16i_kv acc;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = r0 + 4 * kb + j;
-                if (r < R) {
-                    const int64_t o = ((int64_t)hk * R + r) * T + t;
-                    s_out[o] = scale * qs[(int64_t)(r % Mq) * Hq + hk * rep + r / Mq] * kscale * (float)acc[j];
-                    if (dots) dots[o] = acc[j];
-                }
+        for (int i = 0; i < 16; ++i) acc[i] = 0;
+#pragma unroll
+        for (int ks2 = 0; ks2 < 4; ++ks2)
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i *>(qrow + 32 * ks2), b[ks2], acc,
+                                                        0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int rr = 8 * (i >> 2) + 4 * h + (i & 3);  // row within the tile
+            const float sqr = __shfl(sq, rr, 64);
+            const int r = r0 + rr;
+            if (t < T && r < R) {
+                const int64_t o = ((int64_t)hk * R + r) * T + t;
+                s_out[o] = sqr * kscale * (float)acc[i];
+                if (dots) dots[o] = acc[i];
             }
         }
     }
@@ -302,7 +316,7 @@ hipError_t launch_kv_quant(const uint16_t *kv, int64_t T, int H, int64_t ld, int
 hipError_t launch_attn_qk(const int8_t *qq, const float *qs, const int8_t *kq, const float *ks, float scale, int Mq,
                           int T, int Hq, int Hkv, float *s_out, int32_t *dots, hipStream_t s) {
     const int R = Hq / Hkv * Mq;
-    dim3 grid((unsigned)((T + 63) / 64), (unsigned)Hkv, (unsigned)((R + 63) / 64));
+    dim3 grid((unsigned)((T + 127) / 128), (unsigned)Hkv, (unsigned)((R + 63) / 64));
     attn_qk_kernel<<<grid, 256, 0, s>>>(qq, qs, kq, ks, scale, Mq, T, Hq, Hkv, s_out, dots);
     return hipGetLastError();
 }
@@ -312,8 +326,8 @@ PvPlan attn_pv_plan(int64_t Mq, int64_t T, int64_t Hq, int64_t Hkv) {
     const int64_t R = Hq / Hkv * Mq;
     const int64_t tiles = Hkv * ((R + 31) / 32);
     const int64_t B = (T + 127) / 128;
-    // about 512 workgroups (two per compute unit): split the token blocks when the row
-    // tiles alone give fewer
+    // about 512 workgroups (two per compute unit; 256 and 1024 measured slower): split the
+    // token blocks when the row tiles alone give fewer
     int64_t S = tiles >= 512 || B <= 1 ? 1 : std::min<int64_t>(B, (512 + tiles - 1) / tiles);
     const int64_t bps = S > 0 ? (B + S - 1) / std::max<int64_t>(S, 1) : 1;
     S = bps > 0 ? (B + bps - 1) / bps : 1;  // no empty split
