@@ -80,7 +80,11 @@ def _qk_case(Mq, T, Hq, Hkv, seed, scale=128 ** -0.5):
 
 
 @pytest.mark.parametrize("Mq,T,Hq,Hkv", [(8, 2048, 32, 8), (3, 77, 4, 1), (17, 129, 2, 2), (1, 1, 1, 1),
-                                         (64, 300, 8, 8), (8, 16384, 32, 8)])
+                                         (64, 300, 8, 8), (8, 16384, 32, 8),
+                                         (8, 32768, 32, 8),    # the benchmark's long context
+                                         (40, 161, 8, 2),      # 160 rows per KV head: three row blocks
+                                         (3, 200, 32, 1),      # one KV head shared by 32 query heads
+                                         (2, 130, 64, 64)])    # one query head per KV head
 def test_attn_qk_int8(Mq, T, Hq, Hkv):
     s, dots, s_o, d_o = _qk_case(Mq, T, Hq, Hkv, 3)
     assert np.array_equal(dots, d_o), "int32 dots"
@@ -115,7 +119,10 @@ def _pv_check(p, vq, vs, what):
 
 @pytest.mark.parametrize("Mq,T,Hq,Hkv", [(8, 2048, 32, 8), (3, 77, 4, 1), (17, 129, 2, 2), (1, 1, 1, 1),
                                          (20, 300, 8, 4), (8, 16384, 32, 8), (8, 5000, 32, 8), (2, 1000, 4, 4),
-                                         (512, 700, 32, 8)])
+                                         (512, 700, 32, 8),
+                                         (8, 32768, 32, 8),    # the benchmark's long context
+                                         (3, 200, 32, 1),      # 96 rows on one KV head: three row tiles
+                                         (2, 130, 64, 64)])    # one query head per KV head
 def test_attn_pv_int8(Mq, T, Hq, Hkv):
     p = _probs(5, f"p{Mq}x{T}", Hq, Mq, T)
     vq, vs = oracle.kv_quant_block128(_kv(5, f"v{T}", T, Hkv))
