@@ -354,11 +354,12 @@ WoPlan wo_plan(int M, int N, int K) {
     p.chunks = (M + 16 * p.MT - 1) / (16 * p.MT);
     p.tiles = (N + 64 * kWoWaves - 1) / (64 * kWoWaves);
     const int NCH = (K + kWoChunk - 1) / kWoChunk;
-    // Target two workgroups per CU (their LDS rings fit), more for small m chunks; K
-    // splits of at least two chunks each and at most 16 (the last split to arrive sums
-    // all the pieces).
+    // Target two workgroups per CU (their LDS rings fit); four for small m chunks was
+    // slower (longer weight streams per workgroup win: gate_up at M = 8 55.9 -> 48.6 us,
+    // the 8-bit vocabulary head at M = 1 228.7 -> 201.6 us).  K splits of at least two
+    // chunks each and at most 16 (the last split to arrive sums all the pieces).
     const int cus = device_cu_count();
-    const int target = p.MT <= 2 ? 4 * cus : 2 * cus;
+    const int target = 2 * cus;
     int S = (target + p.tiles * p.chunks - 1) / (p.tiles * p.chunks);
     S = std::max(1, std::min(S, std::min(16, NCH / 2)));
     if (p.tiles * p.chunks > kMaxCounters) S = 1;
