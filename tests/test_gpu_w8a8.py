@@ -353,3 +353,24 @@ def test_graph_replays_match_eager(layer):
         assert torch.equal(y, y_eager), f"replay {r}"
         i8.gemm_w8a8_g128(qwo, wso, x=xo)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,K,N,kern", [(64, 1024, 264, "auto"), (300, 2048, 264, "auto"), (100, 512, 136, "tiled")])
+def test_extreme_weight_scales(M, K, N, kern):
+    """Weight scales across the whole range the contract admits, from fp32 subnormals to
+    2^99, mixed per group and column: the decode kernel folds with w_scale * 2^26 (exact for
+    |w_scale| < 2^100), the prefill and tiled kernels with w_scale itself."""
+    xb = synth.activations_bf16(7, f"xs{M}", M, K, True)
+    qw, _ = rtn_weights(7, f"xs{K}x{N}", K, N, 8)
+    G = K // 128
+    g = np.random.Generator(np.random.Philox(key=7))
+    e = g.integers(-149, 99, size=(G, N))                       # subnormal to 2^99
+    ws = (np.ldexp(1.0, e) * g.uniform(1.0, 2.0, size=(G, N))).astype(np.float32)
+    ws[0, :8] = np.float32(2.0 ** -149)                            # the smallest subnormal
+    ws[-1, -8:] = np.float32(np.nextafter(np.float32(2.0 ** 100), np.float32(0)))
+    ws = np.where(np.isfinite(ws), ws, np.float32(1.0)).astype(np.float32)
+    y = i8.gemm_w8a8_g128_ex(dev(qw), dev(ws), x=dev_bf16(xb), kernel=KERNELS[kern])
+    torch.cuda.synchronize()
+    qa, s = oracle.quant_act_per_token(xb)
+    y_exact, T = oracle.gemm_w8a8_g128(qa, s, oracle.gptq_unpack(qw, 8, K), ws)
+    assert_within_tolerance(host_bf16_bits(y), y_exact, T, K, what=f"extreme scales {M}x{K}x{N} {kern}")
