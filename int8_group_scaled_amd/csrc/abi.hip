@@ -99,13 +99,17 @@ int check_ld(int64_t ld, int64_t dim, const char *name) {
 
 size_t w8a8_quant_bytes(int64_t M, int64_t K) { return align256(size_t(M) * size_t(K)) + align256(size_t(M) * 4); }
 
-// Which kernel a 4-bit group-128 weight-only call takes: the register-streaming kernel for
-// wide layers at few tokens (the vocabulary head), where each workgroup streams long runs
-// of K, the LDS-staged W4A16 kernel on the decode layer shapes (measured faster there).
-bool wo_takes_w4(int64_t M, int64_t N) { return M <= 16 && N >= 65536; }
+// Which kernel a weight-only call takes: the register-streaming kernel for wide layers at
+// few tokens (the vocabulary heads), where each workgroup streams long runs of K, and the
+// LDS-staged kernel otherwise (measured faster on the decode layer shapes at 8 and 64
+// rows, for 4-bit and 8-bit codes).
+bool wo_uses_lds(int bits, int64_t M, int64_t N) {
+    (void)bits;
+    return !(M <= 16 && N >= 65536);
+}
 
 size_t w4_or_wo_workspace(int bits, int64_t M, int64_t N, int64_t K) {
-    if (bits == 4 && !wo_takes_w4(M, N)) return w4a16_gemm_workspace((int)M, (int)N, (int)K);
+    if (wo_uses_lds(bits, M, N)) return w4a16_gemm_workspace((int)M, (int)N, (int)K);
     return wo_gemm_workspace((int)M, (int)N, (int)K);
 }
 
@@ -408,10 +412,10 @@ int gemm_weight_only(const void *x, int64_t ldx, const int32_t *qweight, int bit
     }
     I8GS_TRY(check_device());
     char *wsp = (char *)workspace;
-    if (bits == 4 && !wo_takes_w4(M, N)) {
-        // 4-bit group 128 on the decode shapes: the LDS-staged W4A16 kernel (faster there)
+    if (wo_uses_lds(bits, M, N)) {
+        // the decode layer shapes: the LDS-staged kernel (faster there)
         W4A16Args a{(const uint16_t *)x, ldx, qweight, w_scale, (uint16_t *)y, ldy, (int)M, (int)N, (int)K,
-                    part ? (int *)wsp : nullptr, part ? (void *)(wsp + kCounterBytes) : nullptr, part};
+                    part ? (int *)wsp : nullptr, part ? (void *)(wsp + kCounterBytes) : nullptr, part, bits, group};
         I8GS_TRY(hip_check(launch_w4a16_gemm(a, (hipStream_t)stream), "gemm_weight_only launch"));
         return ok();
     }

@@ -115,6 +115,8 @@ struct W4A16Args {
     int *counters;
     void *ws;
     size_t ws_bytes;
+    int bits = 4;     // 4 (group 128) or 8 (group 128 or 32)
+    int group = 128;
 };
 size_t w4a16_gemm_workspace(int M, int N, int K);
 

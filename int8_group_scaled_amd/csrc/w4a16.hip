@@ -1,29 +1,35 @@
-// W4A16 g128 weight-only GEMM on gfx950 bf16 MFMA.
+// LDS-staged weight-only GEMM on gfx950 bf16 MFMA: W4A16 g128 and W8A16 g128 / g32 on the
+// decode and prefill layer shapes (the vocabulary heads at few tokens take the
+// register-streaming kernel of wonly.hip).
 //
 // Qwen3.8-27B-DFlash2-W4A16-g128-sym-GPTQ model card, property table (W4A16,
 // group_size 128, symmetric) and quantised-layer table (all attention / MLP
-// linears and fc in INT4 g128 sym).  y[m,n] = bf16(sum_g w_scale[g,n] *
-// sum_{k in g} x[m,k] * q[k,n]) with q = nibble - 8.
+// linears and fc in INT4 g128 sym); Qwen3.5-4B-DFlash-W8A16 model card (int8 weights,
+// bf16 activations); qwen38/dflash2 recipe, quantisation settings (int8 projections at
+// group 32).  y[m,n] = bf16(sum_g w_scale[g,n] * sum_{k in g} x[m,k] * q[k,n]) with
+// q = code - 2^(bits-1).
 //
-// Each nibble is turned into the exact bf16 value of 16*q (q an integer in [-8, 7]):
-// masking a word's high nibbles in place, or its low nibbles shifted up by 4, and
-// flipping bit 7 of every byte leaves 16*q as a signed byte; a sign-extending byte
-// convert (SDWA) gives the fp32 value, whose top half is its bf16 pattern.  One
-// 128-wide group is summed by four v_mfma_f32_16x16x32_bf16 into a fresh fp32
-// accumulator (the products are exact in fp32), then scaled by that group's
-// per-column scale / 16 (exact) and added to the running fp32 sum.  Scaling after
-// the group keeps the error relative to sum |x*q| rather than to the cancelling
+// 4 bits: each nibble is turned into the exact bf16 value of 16*q (q an integer in
+// [-8, 7]): masking a word's high nibbles in place, or its low nibbles shifted up by 4,
+// and flipping bit 7 of every byte leaves 16*q as a signed byte; a sign-extending byte
+// convert (SDWA) gives the fp32 value, whose top half is its bf16 pattern.  8 bits: XOR
+// 0x80 per byte leaves q itself as a signed byte, converted the same way.  One 128-wide
+// group (or, at group 32, each 32-wide K step) is summed by v_mfma_f32_16x16x32_bf16 into
+// a fresh fp32 accumulator (the products are exact in fp32), then scaled by that group's
+// per-column scale (/ 16 at 4 bits, exact) and added to the running fp32 sum.  Scaling
+// after the group keeps the error relative to sum |x*q| rather than to the cancelling
 // scaled terms.
 //
 // MFMA layout (16x16x32 bf16): lane l holds row (l % 16) of A and column (l % 16)
 // of B, 8 consecutive K values starting at 8 * (l / 16) within the 32-wide K step;
-// with GPTQ's packing those 8 values of one column are exactly one int32 word.
+// with GPTQ's packing those 8 values of one column are exactly one int32 word at 4 bits
+// and two consecutive words at 8 bits.
 //
 // Data flow (as in the W8A8 decode kernel): a workgroup of 8 waves owns a tile of
 // 128 columns (16 per wave) and up to 64 rows, and walks its K groups through a
 // D-stage LDS ring filled by buffer_load ... lds copies -- a stage holds the group's
-// 16 packed weight rows of the tile, its activation rows (bf16, 256 bytes each) and
-// the tile's scales -- with the wait for a stage issued D - 2 stages behind the
+// 16 (4 bits) or 32 (8 bits) packed weight rows of the tile, its activation rows (bf16,
+// 256 bytes each) and the tile's scales -- with the wait for a stage issued D - 2 stages behind the
 // copies, so D - 1 groups are in flight.  K is split across S workgroups when the
 // column tiles alone cannot fill the GPU; the splits publish fp32 partials with
 // device-coherent stores and the last to arrive sums them in split order.  Rows
@@ -55,61 +61,108 @@ __device__ __forceinline__ v4f mfma_bf16(v4i a, v8bf b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), b, c, 0, 0, 0);
 }
 
-// Stage layout (bytes): the 16 x 128 weight words, row-major, with the 16-byte pieces
-// of packed row r permuted by XOR with 4 * (r % 4) (a B read's four lane groups read
-// rows 4 apart: they land in different banks); then the activation rows, 256 bytes
-// each, pieces permuted by XOR with row % 16; then the 128 scales.
-template <int MT>
+// Stage layout (bytes): the PR x 128 weight words of one 128-wide K group (PR = 16
+// packed rows at 4 bits, 32 at 8 bits), row-major, with the 16-byte pieces of packed
+// row r permuted by XOR with swz(r) (a B read's four lane groups read rows that land in
+// different banks); then the activation rows, 256 bytes each, pieces permuted by XOR
+// with row % 16; then the 128 scales of each of the group's 128/GS scale rows.
+template <int BITS, int GS, int MT>
 struct W4Stage {
+    static_assert((BITS == 4 && GS == 128) || (BITS == 8 && (GS == 128 || GS == 32)), "weight-only LDS shape");
+    static constexpr int PR = 128 * BITS / 32;              // packed rows per group
     static constexpr int ROWS = 16 * MT;
-    static constexpr int WB = 16 * kTN * 4;
+    static constexpr int WB = PR * kTN * 4;
     static constexpr int AB = ROWS * 256;
-    static constexpr int SB = kTN * 4;
+    static constexpr int NSG = 128 / GS;                     // scale rows per stage
+    static constexpr int SB = NSG * kTN * 4;
     static constexpr int BYTES = WB + AB + SB;
+    static constexpr int WPW = PR / 16;                      // 1 KiB weight copies per wave (8 waves)
     static constexpr int ACOPIES = AB / 1024;              // 1 KiB activation copies per stage
     static constexpr int AI = (ACOPIES + 7) / 8;           // per wave (extra ones repeat the last)
+    static constexpr int SPW = NSG == 1 ? 1 : 2;             // 256-byte scale copies per copying wave
 };
 
-// The copies of one stage (group g) by this wave.
-template <int MT>
+// Piece permutation of packed row r: rows 4 apart (4 bits: a lane group's row 4*ks +
+// lb) or 2 apart (8 bits: rows 8*ks + 2*lb and the next) are spread over the banks.
+template <int BITS>
+__device__ __forceinline__ int w4_swz(int r) {
+    return BITS == 4 ? ((r & 3) << 2) : (((r >> 1) & 3) << 2);
+}
+
+// The copies of one stage (group g) by this wave: its WPW weight copies (packed rows
+// 2*(WPW*wave + j) and the next), its activation copies and its scale copies (4 bits:
+// half wave % 2 of the tile's 128 scales; group 32: both halves of scale row wave).
+template <int BITS, int GS, int MT>
 __device__ __forceinline__ void w4_issue(char *st, int g, int wave, int N, __amdgpu_buffer_rsrc_t wr,
-                                         __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t sr, int w_voff,
-                                         const int (&a_voff)[W4Stage<MT>::AI], const int (&a_ins)[W4Stage<MT>::AI],
-                                         int s_half, int s_voff) {
-    using SG = W4Stage<MT>;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + wave * 1024), 16, w_voff,
-                                             (int)((uint32_t)g * 16u * (uint32_t)N * 4u), 0, kCpolNT);
+                                         __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t sr,
+                                         const int (&w_voff)[W4Stage<BITS, GS, MT>::WPW],
+                                         const int (&a_voff)[W4Stage<BITS, GS, MT>::AI],
+                                         const int (&a_ins)[W4Stage<BITS, GS, MT>::AI], int s_half, int s_voff) {
+    using SG = W4Stage<BITS, GS, MT>;
+#pragma unroll
+    for (int j = 0; j < SG::WPW; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + (wave * SG::WPW + j) * 1024), 16, w_voff[j],
+                                                 (int)((uint32_t)g * (uint32_t)SG::PR * (uint32_t)N * 4u), 0, kCpolNT);
 #pragma unroll
     for (int j = 0; j < SG::AI; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, I8GS_LDS(st + SG::WB + a_ins[j] * 1024), 16, a_voff[j], g * 256,
                                                  0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, I8GS_LDS(st + SG::WB + SG::AB + s_half * 256), 4, s_voff,
-                                             (int)((uint32_t)g * (uint32_t)N * 4u), 0, 0);
+    if constexpr (SG::NSG == 1) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, I8GS_LDS(st + SG::WB + SG::AB + s_half * 256), 4, s_voff,
+                                                 (int)((uint32_t)g * (uint32_t)N * 4u), 0, 0);
+    } else {
+        // scale row wave (of NSG = 4), both halves: s_voff addresses the first half
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                sr, I8GS_LDS(st + SG::WB + SG::AB + wave * 512 + h * 256), 4, s_voff + h * 256,
+                (int)(((uint32_t)g * (uint32_t)SG::NSG + (uint32_t)wave) * (uint32_t)N * 4u), 0, 0);
+    }
 }
 
-// The copies of wave + 4's share, issued by wave (0-3) too: its weight rows lie 8
+// The copies of wave + 4's share, issued by wave (0-3) too: its weight rows lie 8*WPW
 // further down, its activation copies are given by a_voff / a_ins (its scales repeat
-// those of this wave and are not copied again).
-template <int MT>
+// those of this wave, or are copied by waves 0-3 themselves, and are not copied again).
+template <int BITS, int GS, int MT>
 __device__ __forceinline__ void w4_issue_partner(char *st, int g, int wave, int N, __amdgpu_buffer_rsrc_t wr,
-                                                 __amdgpu_buffer_rsrc_t xr, int w_voff,
-                                                 const int (&a_voff)[W4Stage<MT>::AI],
-                                                 const int (&a_ins)[W4Stage<MT>::AI]) {
-    using SG = W4Stage<MT>;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + (wave + 4) * 1024), 16, w_voff,
-                                             (int)(((uint32_t)g * 16u + 8u) * (uint32_t)N * 4u), 0, kCpolNT);
+                                                 __amdgpu_buffer_rsrc_t xr,
+                                                 const int (&w_voff)[W4Stage<BITS, GS, MT>::WPW],
+                                                 const int (&a_voff)[W4Stage<BITS, GS, MT>::AI],
+                                                 const int (&a_ins)[W4Stage<BITS, GS, MT>::AI]) {
+    using SG = W4Stage<BITS, GS, MT>;
+#pragma unroll
+    for (int j = 0; j < SG::WPW; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wr, I8GS_LDS(st + ((wave + 4) * SG::WPW + j) * 1024), 16, w_voff[j],
+            (int)(((uint32_t)g * (uint32_t)SG::PR + 8u * (uint32_t)SG::WPW) * (uint32_t)N * 4u), 0, kCpolNT);
 #pragma unroll
     for (int j = 0; j < SG::AI; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, I8GS_LDS(st + SG::WB + a_ins[j] * 1024), 16, a_voff[j], g * 256,
                                                  0, 0);
 }
 
-template <int MT, int D>
+// The 8 codes of two 8-bit words (K order: word 0 bytes 0..3, word 1 bytes 0..3) as
+// bf16 of q = code - 128: XOR 0x80 per byte makes q a signed byte, a sign-extending
+// byte convert gives the exact fp32 value, whose top half is its bf16 pattern.
+__device__ __forceinline__ v8bf dequant8x8(uint32_t w0, uint32_t w1) {
+    v4i out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = (i < 2 ? w0 : w1) ^ 0x80808080u;
+        const int sh = 16 * (i & 1);
+        const uint32_t fe = __float_as_uint((float)(signed char)(w >> sh));
+        const uint32_t fo = __float_as_uint((float)(signed char)(w >> (sh + 8)));
+        out[i] = (int)__builtin_amdgcn_perm(fo, fe, 0x07060302u);  // top halves: (fe >> 16) | (fo & 0xFFFF0000)
+    }
+    return __builtin_bit_cast(v8bf, out);
+}
+
+template <int BITS, int GS, int MT, int D>
 __global__ __launch_bounds__(512) void w4a16_stream_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, const int32_t *__restrict__ qweight,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ldy, int M, int N, int K, int S,
     int tiles, float *__restrict__ part, size_t part_bytes, int *__restrict__ cnt) {
-    using SG = W4Stage<MT>;
+    using SG = W4Stage<BITS, GS, MT>;
     constexpr int RING = D * SG::BYTES;
     // One LDS object only (see the W8A8 decode kernel); the split flag sits after the ring.
     __shared__ __attribute__((aligned(1024))) char lds[RING + 16];
@@ -133,12 +186,12 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
     // byte offsets fit 32 bits: K*N < 2^32 is checked before launch, and x is
     // addressed from this chunk's first row
     const uint16_t *xc = x + (int64_t)m0 * ldx;
-    const __amdgpu_buffer_rsrc_t wr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)qweight, 0, (int)((uint32_t)K / 8u * (uint32_t)N * 4u), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)qweight, 0, (int)((uint32_t)K / (32u / BITS) * (uint32_t)N * 4u), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)xc, 0, (int)(((uint32_t)(mrows - 1) * (uint32_t)ldx + (uint32_t)K) * 2u), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t sr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)w_scale, 0, (int)((uint32_t)G * (uint32_t)N * 4u), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)w_scale, 0, (int)((uint32_t)K / (uint32_t)GS * (uint32_t)N * 4u), kRsrcWord3);
 
     // Copy roles.  The shares are per wave w: weights: packed rows 2w, 2w+1 (32 pieces of
     // 4 columns each); activations: copies a_ins; scales: half w % 2.  Waves 0-3 issue
@@ -146,11 +199,12 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
     // older of its two waves, and the copies' issue stalls then fall on the favoured one
     // (1-4% faster on six of the eight decode cases, the other two unchanged).  Every
     // copying wave issues LPSW copies per stage, so one wait count serves all.
-    int w_voff;
-    {
-        const int r = 2 * wave + (lane >> 5), sl = lane & 31;
-        const int piece = sl ^ ((r & 3) << 2);
-        w_voff = (int)(((uint32_t)r * (uint32_t)N + (uint32_t)min(n0 + 4 * piece, N - 4)) * 4u);
+    int w_voff[SG::WPW];
+#pragma unroll
+    for (int j = 0; j < SG::WPW; ++j) {
+        const int r = 2 * (SG::WPW * wave + j) + (lane >> 5), sl = lane & 31;
+        const int piece = sl ^ w4_swz<BITS>(r);
+        w_voff[j] = (int)(((uint32_t)r * (uint32_t)N + (uint32_t)min(n0 + 4 * piece, N - 4)) * 4u);
     }
     // Activations: copy c fills rows 4c .. 4c+3 (16 pieces each); rows past the chunk
     // repeat its last row (never stored).
@@ -170,9 +224,10 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
         const int piece = sl ^ (row & 15);
         a_voffp[j] = (int)(((uint32_t)min(row, mrows - 1) * (uint32_t)ldx + (uint32_t)piece * 8u) * 2u);
     }
-    constexpr int LPSW = 2 * (1 + SG::AI) + 1;
-    // Scales: half k = wave % 2 of the tile's 128 (waves 2..7 repeat them).
-    const int s_half = wave & 1;
+    constexpr int LPSW = 2 * (SG::WPW + SG::AI) + SG::SPW;
+    // Scales (one row per group): half k = wave % 2 of the tile's 128 (waves 2..7 repeat
+    // them).  Group 32: scale row wave of the stage's four, both halves from s_voff.
+    const int s_half = SG::NSG == 1 ? wave & 1 : 0;
     const int s_voff = min(n0 + 64 * s_half + lane, N - 1) * 4;
 
     float acc[MT][4];
@@ -184,18 +239,23 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
 #pragma unroll
     for (int k = 0; k < D - 1; ++k)
         if (k < ng && wave < 4) {
-            w4_issue<MT>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, sr, w_voff, a_voff, a_ins, s_half, s_voff);
-            w4_issue_partner<MT>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, w_voff, a_voffp, a_insp);
+            w4_issue<BITS, GS, MT>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, sr, w_voff, a_voff, a_ins, s_half,
+                                   s_voff);
+            w4_issue_partner<BITS, GS, MT>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, w_voff, a_voffp, a_insp);
         }
 
-    // This lane's B words: column 16*wave + li of packed rows 4*ks + lb.
+    // This lane's B words: column 16*wave + li of packed row 4*ks + lb (4 bits) or of
+    // packed rows 8*ks + 2*lb and the next (8 bits): the K values 32*ks + 8*lb .. +7.
     const int cl = 16 * wave + li;
-    int b_off[4];
+    constexpr int BW = BITS == 4 ? 1 : 2;
+    int b_off[4][BW];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int r = 4 * ks + lb;
-        b_off[ks] = (r * kTN + (((cl >> 2) ^ ((r & 3) << 2)) << 2) + (cl & 3)) * 4;
-    }
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < BW; ++e) {
+            const int r = BITS == 4 ? 4 * ks + lb : 8 * ks + 2 * lb + e;
+            b_off[ks][e] = (r * kTN + (((cl >> 2) ^ w4_swz<BITS>(r)) << 2) + (cl & 3)) * 4;
+        }
     int slot = 0;
     for (int u = 0; u < ng; ++u) {
         // Copies complete in issue order and the next D-2 stages are the youngest ones.
@@ -205,8 +265,8 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
         __builtin_amdgcn_sched_barrier(0);
         if (u + D - 1 < ng && wave < 4) {
             char *const nst = lds + (slot == 0 ? D - 1 : slot - 1) * SG::BYTES;
-            w4_issue<MT>(nst, g0 + u + D - 1, wave, N, wr, xr, sr, w_voff, a_voff, a_ins, s_half, s_voff);
-            w4_issue_partner<MT>(nst, g0 + u + D - 1, wave, N, wr, xr, w_voff, a_voffp, a_insp);
+            w4_issue<BITS, GS, MT>(nst, g0 + u + D - 1, wave, N, wr, xr, sr, w_voff, a_voff, a_ins, s_half, s_voff);
+            w4_issue_partner<BITS, GS, MT>(nst, g0 + u + D - 1, wave, N, wr, xr, w_voff, a_voffp, a_insp);
         }
         __builtin_amdgcn_sched_barrier(0);
         const char *st = lds + slot * SG::BYTES;
@@ -219,26 +279,45 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
         __builtin_amdgcn_s_setprio(1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) bw[ks] = dequant8x16((uint32_t)*reinterpret_cast<const int *>(st + b_off[ks]));
+        for (int ks = 0; ks < 4; ++ks) {
+            if constexpr (BITS == 4)
+                bw[ks] = dequant8x16((uint32_t)*reinterpret_cast<const int *>(st + b_off[ks][0]));
+            else
+                bw[ks] = dequant8x8((uint32_t)*reinterpret_cast<const int *>(st + b_off[ks][0]),
+                                    (uint32_t)*reinterpret_cast<const int *>(st + b_off[ks][1]));
+        }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         v4f p[MT];
+        const float *const srow = reinterpret_cast<const float *>(st + SG::WB + SG::AB);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const v8bf b = bw[ks];
+            // group 32: every K step is a group of its own (a fresh sum, folded below)
+            const bool fresh = ks == 0 || SG::NSG == 4;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int row = mt * 16 + li;
                 const v4i a = *reinterpret_cast<const v4i *>(st + SG::WB + row * 256 + (((4 * ks + lb) ^ li) << 4));
-                p[mt] = mfma_bf16(a, b, ks == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : p[mt]);
+                p[mt] = mfma_bf16(a, b, fresh ? v4f{0.f, 0.f, 0.f, 0.f} : p[mt]);
+            }
+            if constexpr (SG::NSG == 4) {
+                const float sc = srow[ks * kTN + cl];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[mt][r] += sc * p[mt][r];
             }
         }
-        const float sc = reinterpret_cast<const float *>(st + SG::WB + SG::AB)[cl] * 0.0625f;  // sums are 16x
+        if constexpr (SG::NSG == 1) {
+            // 4 bits: the sums are of 16*q, the scale takes the 1/16 (exact)
+            const float sc = srow[cl] * (BITS == 4 ? 0.0625f : 1.0f);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[mt][r] += sc * p[mt][r];
+                for (int r = 0; r < 4; ++r) acc[mt][r] += sc * p[mt][r];
+        }
         slot = slot == D - 1 ? 0 : slot + 1;
     }
 
@@ -341,16 +420,28 @@ W4Plan w4_plan(int M, int N, int K) {
 }
 
 // As many stages as fit in 80 KiB (two workgroups per CU), at most 6.
-template <int MT, int D>
+template <int BITS, int GS, int MT>
 hipError_t launch_w4_mt(const W4A16Args &a, const W4Plan &p, hipStream_t st) {
-    static_assert(D * W4Stage<MT>::BYTES + 16 <= 80 * 1024 && (D == 6 || (D + 1) * W4Stage<MT>::BYTES + 16 > 80 * 1024),
-                  "stage count must be the largest that fits 80 KiB");
+    constexpr int FIT = (80 * 1024 - 16) / W4Stage<BITS, GS, MT>::BYTES;
+    constexpr int D = FIT < 6 ? FIT : 6;
+    static_assert(D >= 2, "at least two stages");
     int *cnt = p.S > 1 ? a.counters : nullptr;
     float *part = p.S > 1 ? (float *)a.ws : nullptr;
     dim3 grid(p.blocks, p.chunks);
-    w4a16_stream_kernel<MT, D><<<grid, 512, 0, st>>>(a.x, a.ldx, a.qweight, a.w_scale, a.y, a.ldy, a.M, a.N, a.K,
-                                                    p.S, p.tiles, part, p.S > 1 ? a.ws_bytes : 0, cnt);
+    w4a16_stream_kernel<BITS, GS, MT, D><<<grid, 512, 0, st>>>(a.x, a.ldx, a.qweight, a.w_scale, a.y, a.ldy, a.M,
+                                                              a.N, a.K, p.S, p.tiles, part,
+                                                              p.S > 1 ? a.ws_bytes : 0, cnt);
     return hipGetLastError();
+}
+
+template <int BITS, int GS>
+hipError_t launch_w4_bits(const W4A16Args &a, const W4Plan &p, hipStream_t s) {
+    switch (p.MT) {
+        case 1: return launch_w4_mt<BITS, GS, 1>(a, p, s);
+        case 2: return launch_w4_mt<BITS, GS, 2>(a, p, s);
+        case 3: return launch_w4_mt<BITS, GS, 3>(a, p, s);
+        default: return launch_w4_mt<BITS, GS, 4>(a, p, s);
+    }
 }
 
 }  // namespace
@@ -364,12 +455,8 @@ size_t w4a16_gemm_workspace(int M, int N, int K) {
 
 hipError_t launch_w4a16_gemm(const W4A16Args &a, hipStream_t s) {
     const W4Plan p = w4_plan(a.M, a.N, a.K);
-    switch (p.MT) {
-        case 1: return launch_w4_mt<1, 6>(a, p, s);
-        case 2: return launch_w4_mt<2, 4>(a, p, s);
-        case 3: return launch_w4_mt<3, 3>(a, p, s);
-        default: return launch_w4_mt<4, 3>(a, p, s);
-    }
+    if (a.bits == 8) return a.group == 32 ? launch_w4_bits<8, 32>(a, p, s) : launch_w4_bits<8, 128>(a, p, s);
+    return launch_w4_bits<4, 128>(a, p, s);
 }
 
 }  // namespace i8gs

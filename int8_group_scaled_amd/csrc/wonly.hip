@@ -1,4 +1,7 @@
-// Weight-only group-scaled GEMM on gfx950 bf16 MFMA: W4A16 g128 and W8A16 g128 / g32.
+// Weight-only group-scaled GEMM on gfx950 bf16 MFMA: W4A16 g128 and W8A16 g128 / g32,
+// register-streamed.  Calls of up to 16 rows on layers of at least 65536 columns (the
+// vocabulary heads) take this kernel; the others take the LDS-staged kernel in
+// w4a16.hip, faster on the decode layer shapes.
 //
 // Qwen3.8-27B-DFlash2-W4A16-g128-sym-GPTQ model card, property and quantised-layer
 // tables (4-bit weights, bf16 activations, group 128, symmetric); Qwen3.5-4B-DFlash-
