@@ -59,9 +59,9 @@ HBM_PEAK_GBS = 8000.0
 # is reported as null.
 DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h")
 DECODE_TRAFFIC = {
-    "sources_sha256": "f72b723771a8b93769b6ae71bafdda6e0d5a9e3aec764757f6fbba467268f946",
-    "fetch": {"qkv": 36823840, "o_proj": 26537984, "gate_up": 192127328, "down": 107585504},
-    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456456, "down": 8528640},
+    "sources_sha256": "3f2706a24a67c1d57b433f24187ab53086f3515c88c665dc65d9abdc7bb4f0f0",
+    "fetch": {"qkv": 36819660, "o_proj": 26534833, "gate_up": 189721794, "down": 107572700},
+    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456448, "down": 8528640},
 }
 EVENT_EVERY = 8  # per-kernel HIP events on every 8th timed step (each event adds a gap)
 INT8_PEAK_TOPS = 5000.0
