@@ -57,8 +57,8 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t *__restric
 // form R = (Hq/Hkv) * Mq rows r = (h - hk*Hq/Hkv) * Mq + i; row r is row hk*R + r of
 // the [Hq*Mq, ...] score, probability and output matrices.
 
-// QK: a workgroup covers 128 tokens (32 per wave) and up to 64 rows of one group (two
-// 32-row tiles).  A wave loads its tokens' K vectors once as the B operand of
+// QK: a workgroup covers 32 tokens per wave (four waves, fewer for short contexts) and
+// up to 64 rows of one group (two 32-row tiles).  A wave loads its tokens' K vectors once as the B operand of
 // v_mfma_i32_32x32x32_i8 (lane l: token l % 32, 16 bytes of the head dimension at
 // 16*(l/32) + 32*step, four steps) and multiplies them with each row tile's query
 // vectors (the A operand, the same byte placement).  Register i of the result holds
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void attn_qk_kernel(const int8_t *__restrict__
                                                       float *__restrict__ s_out, int32_t *__restrict__ dots) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int hk = blockIdx.y, rep = Hq / Hkv, R = rep * Mq;
-    const int t0 = blockIdx.x * 128 + wave * 32;
+    const int t0 = (blockIdx.x * (blockDim.x >> 6) + wave) * 32;
     if (t0 >= T) return;
     const int li = lane & 31, h = lane >> 5;
     const int kt = min(t0 + li, T - 1);  // tokens past the end: never stored
@@ -316,8 +316,13 @@ hipError_t launch_kv_quant(const uint16_t *kv, int64_t T, int H, int64_t ld, int
 hipError_t launch_attn_qk(const int8_t *qq, const float *qs, const int8_t *kq, const float *ks, float scale, int Mq,
                           int T, int Hq, int Hkv, float *s_out, int32_t *dots, hipStream_t s) {
     const int R = Hq / Hkv * Mq;
-    dim3 grid((unsigned)((T + 127) / 128), (unsigned)Hkv, (unsigned)((R + 63) / 64));
-    attn_qk_kernel<<<grid, 256, 0, s>>>(qq, qs, kq, ks, scale, Mq, T, Hq, Hkv, s_out, dots);
+    // 32 tokens per wave; four waves per workgroup, or fewer when that leaves fewer than
+    // about two workgroups per compute unit (short contexts)
+    const int64_t others = (int64_t)Hkv * ((R + 63) / 64);
+    int waves = 4;
+    while (waves > 1 && (T + 32 * waves - 1) / (32 * waves) * others < 512) waves >>= 1;
+    dim3 grid((unsigned)((T + 32 * waves - 1) / (32 * waves)), (unsigned)Hkv, (unsigned)((R + 63) / 64));
+    attn_qk_kernel<<<grid, 64 * waves, 0, s>>>(qq, qs, kq, ks, scale, Mq, T, Hq, Hkv, s_out, dots);
     return hipGetLastError();
 }
 
