@@ -660,15 +660,29 @@ def main():
         oracle_linear(xb, qw, sc, L)
         t_qkv = time.perf_counter() - ta
         oracle.set_num_threads(threads)
+        # prefill: the qkv layer at M = 4096, exact group sums and fold for 64 sampled rows
+        PL = synth.LAYERS["qkv"]
+        qa_p = np.maximum(synth.uniform_words(0, "bench-prefill-cpu", 4096 * PL.K // 4).view(np.int8), -127)
+        qa_p = qa_p.reshape(4096, PL.K)
+        s_p = np.abs(synth.normal_f32(0, "bench-prefill-cpu-s", 4096)) + 1e-3
+        q_p = oracle.gptq_unpack(host[0][1], 8, PL.K)
+        rows_p = synth.sample_rows(0, "bench-prefill-cpu", 4096, 64)
+        ta = time.perf_counter()
+        oracle.gemm_w8a8_g128(qa_p, s_p, q_p, host[0][2], rows=rows_p)
+        t_pf = time.perf_counter() - ta
+        pf_tops = 2.0 * len(rows_p) * PL.N * PL.K / t_pf / 1e12
         out["cpu_baseline"] = {"value": round(cpu_gbs, 3), "unit": "GB/s", "cores": threads,
                                "kind": "oracle",
                                "sample": f"the full decode step (64 tokens x 4 layers: quantise, unpack, exact "
                                          f"group sums, fold, bf16) repeated {reps}x in {el:.1f}s",
                                "per_layer_GBps": per_layer_cpu,
                                "single_thread": {"single_linear_8x512x256_ms": round(t_single * 1e3, 3),
-                                                 "qkv_64x5120x6144_s": round(t_qkv, 3)}}
+                                                 "qkv_64x5120x6144_s": round(t_qkv, 3)},
+                               "prefill_TOPS": round(pf_tops, 4),
+                               "prefill_sample": f"qkv 5120->6144 at M=4096, 64 sampled rows (exact group sums "
+                                                 f"and fold, {threads} threads) in {t_pf:.2f}s"}
         log(f"cpu oracle: {cpu_gbs:.2f} GB/s on {threads} threads; single thread: single linear "
-            f"{t_single * 1e3:.2f} ms, qkv {t_qkv:.2f} s")
+            f"{t_single * 1e3:.2f} ms, qkv {t_qkv:.2f} s; prefill sample {pf_tops:.3f} TOP/s")
 
     print(json.dumps(out), flush=True)
 
