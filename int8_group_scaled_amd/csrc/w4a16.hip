@@ -34,6 +34,8 @@
 // column tiles alone cannot fill the GPU; the splits publish fp32 partials with
 // device-coherent stores and the last to arrive sums them in split order.  Rows
 // are processed in chunks of 64 (gridDim.y).
+#include <algorithm>
+
 #include "internal.h"
 
 namespace i8gs {
@@ -61,24 +63,30 @@ __device__ __forceinline__ v4f mfma_bf16(v4i a, v8bf b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), b, c, 0, 0, 0);
 }
 
-// Stage layout (bytes): the PR x 128 weight words of one 128-wide K group (PR = 16
-// packed rows at 4 bits, 32 at 8 bits), row-major, with the 16-byte pieces of packed
-// row r permuted by XOR with swz(r) (a B read's four lane groups read rows that land in
-// different banks); then the activation rows, 256 bytes each, pieces permuted by XOR
-// with row % 16; then the 128 scales of each of the group's 128/GS scale rows.
-template <int BITS, int GS, int MT>
+// Stage layout (bytes): the PR x 128 weight words of KS 32-wide K steps (one 128-wide
+// group: PR = 16 packed rows at 4 bits, 32 at 8 bits; two groups at 4 bits with KS = 8),
+// row-major, with the 16-byte pieces of packed row r permuted by XOR with swz(r) (a B
+// read's four lane groups read rows that land in different banks); then the activation
+// rows, 2 * 32 * KS bytes each, pieces permuted by XOR with row % 16; then the 128 scales
+// of each of the stage's scale rows.
+template <int BITS, int GS, int MT, int KS = 4>
 struct W4Stage {
-    static_assert((BITS == 4 && GS == 128) || (BITS == 8 && (GS == 128 || GS == 32)), "weight-only LDS shape");
-    static constexpr int PR = 128 * BITS / 32;              // packed rows per group
+    static_assert((BITS == 4 && GS == 128 && (KS == 4 || KS == 8)) ||
+                      (BITS == 8 && (GS == 128 || GS == 32) && KS == 4),
+                  "weight-only LDS shape");
+    static constexpr int KPS = 32 * KS;                      // K values per stage (KS MFMA K steps)
+    static constexpr int PR = KPS * BITS / 32;               // packed rows per stage
     static constexpr int ROWS = 16 * MT;
+    static constexpr int ROWB = KPS * 2;                     // bytes of one activation row
     static constexpr int WB = PR * kTN * 4;
-    static constexpr int AB = ROWS * 256;
-    static constexpr int NSG = 128 / GS;                     // scale rows per stage
+    static constexpr int AB = ROWS * ROWB;
+    static constexpr int NSG = KPS / GS;                     // scale rows per stage
     static constexpr int SB = NSG * kTN * 4;
     static constexpr int BYTES = WB + AB + SB;
     static constexpr int WPW = PR / 16;                      // 1 KiB weight copies per wave (8 waves)
     static constexpr int ACOPIES = AB / 1024;              // 1 KiB activation copies per stage
     static constexpr int AI = (ACOPIES + 7) / 8;           // per wave (extra ones repeat the last)
+    static constexpr int RPC = 1024 / ROWB;                  // activation rows per copy
     static constexpr int SPW = NSG == 1 ? 1 : 2;             // 256-byte scale copies per copying wave
 };
 
@@ -89,47 +97,50 @@ __device__ __forceinline__ int w4_swz(int r) {
     return BITS == 4 ? ((r & 3) << 2) : (((r >> 1) & 3) << 2);
 }
 
-// The copies of one stage (group g) by this wave: its WPW weight copies (packed rows
-// 2*(WPW*wave + j) and the next), its activation copies and its scale copies (4 bits:
-// half wave % 2 of the tile's 128 scales; group 32: both halves of scale row wave).
-template <int BITS, int GS, int MT>
+// The copies of one stage (stage g) by this wave: its WPW weight copies (packed rows
+// 2*(WPW*wave + j) and the next), its activation copies and its scale copies (one scale
+// row: half wave % 2 of the tile's 128 scales; several: both halves of scale row
+// wave % NSG).
+template <int BITS, int GS, int MT, int KS>
 __device__ __forceinline__ void w4_issue(char *st, int g, int wave, int N, __amdgpu_buffer_rsrc_t wr,
                                          __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t sr,
-                                         const int (&w_voff)[W4Stage<BITS, GS, MT>::WPW],
-                                         const int (&a_voff)[W4Stage<BITS, GS, MT>::AI],
-                                         const int (&a_ins)[W4Stage<BITS, GS, MT>::AI], int s_half, int s_voff) {
-    using SG = W4Stage<BITS, GS, MT>;
+                                         const int (&w_voff)[W4Stage<BITS, GS, MT, KS>::WPW],
+                                         const int (&a_voff)[W4Stage<BITS, GS, MT, KS>::AI],
+                                         const int (&a_ins)[W4Stage<BITS, GS, MT, KS>::AI], int s_half, int s_voff) {
+    using SG = W4Stage<BITS, GS, MT, KS>;
 #pragma unroll
     for (int j = 0; j < SG::WPW; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + (wave * SG::WPW + j) * 1024), 16, w_voff[j],
                                                  (int)((uint32_t)g * (uint32_t)SG::PR * (uint32_t)N * 4u), 0, kCpolNT);
 #pragma unroll
     for (int j = 0; j < SG::AI; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, I8GS_LDS(st + SG::WB + a_ins[j] * 1024), 16, a_voff[j], g * 256,
-                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, I8GS_LDS(st + SG::WB + a_ins[j] * 1024), 16, a_voff[j],
+                                                 g * SG::ROWB, 0, 0);
     if constexpr (SG::NSG == 1) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, I8GS_LDS(st + SG::WB + SG::AB + s_half * 256), 4, s_voff,
                                                  (int)((uint32_t)g * (uint32_t)N * 4u), 0, 0);
     } else {
-        // scale row wave (of NSG = 4), both halves: s_voff addresses the first half
+        // scale row wave % NSG, both halves: s_voff addresses the first half (with two
+        // scale rows, waves 2 and 3 copy the same bytes as waves 0 and 1)
+        const int sri = wave % SG::NSG;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                sr, I8GS_LDS(st + SG::WB + SG::AB + wave * 512 + h * 256), 4, s_voff + h * 256,
-                (int)(((uint32_t)g * (uint32_t)SG::NSG + (uint32_t)wave) * (uint32_t)N * 4u), 0, 0);
+                sr, I8GS_LDS(st + SG::WB + SG::AB + sri * 512 + h * 256), 4, s_voff + h * 256,
+                (int)(((uint32_t)g * (uint32_t)SG::NSG + (uint32_t)sri) * (uint32_t)N * 4u), 0, 0);
     }
 }
 
 // The copies of wave + 4's share, issued by wave (0-3) too: its weight rows lie 8*WPW
 // further down, its activation copies are given by a_voff / a_ins (its scales repeat
 // those of this wave, or are copied by waves 0-3 themselves, and are not copied again).
-template <int BITS, int GS, int MT>
+template <int BITS, int GS, int MT, int KS>
 __device__ __forceinline__ void w4_issue_partner(char *st, int g, int wave, int N, __amdgpu_buffer_rsrc_t wr,
                                                  __amdgpu_buffer_rsrc_t xr,
-                                                 const int (&w_voff)[W4Stage<BITS, GS, MT>::WPW],
-                                                 const int (&a_voff)[W4Stage<BITS, GS, MT>::AI],
-                                                 const int (&a_ins)[W4Stage<BITS, GS, MT>::AI]) {
-    using SG = W4Stage<BITS, GS, MT>;
+                                                 const int (&w_voff)[W4Stage<BITS, GS, MT, KS>::WPW],
+                                                 const int (&a_voff)[W4Stage<BITS, GS, MT, KS>::AI],
+                                                 const int (&a_ins)[W4Stage<BITS, GS, MT, KS>::AI]) {
+    using SG = W4Stage<BITS, GS, MT, KS>;
 #pragma unroll
     for (int j = 0; j < SG::WPW; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -137,8 +148,8 @@ __device__ __forceinline__ void w4_issue_partner(char *st, int g, int wave, int 
             (int)(((uint32_t)g * (uint32_t)SG::PR + 8u * (uint32_t)SG::WPW) * (uint32_t)N * 4u), 0, kCpolNT);
 #pragma unroll
     for (int j = 0; j < SG::AI; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, I8GS_LDS(st + SG::WB + a_ins[j] * 1024), 16, a_voff[j], g * 256,
-                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, I8GS_LDS(st + SG::WB + a_ins[j] * 1024), 16, a_voff[j],
+                                                 g * SG::ROWB, 0, 0);
 }
 
 // The 8 codes of two 8-bit words (K order: word 0 bytes 0..3, word 1 bytes 0..3) as
@@ -157,12 +168,12 @@ __device__ __forceinline__ v8bf dequant8x8(uint32_t w0, uint32_t w1) {
     return __builtin_bit_cast(v8bf, out);
 }
 
-template <int BITS, int GS, int MT, int D>
+template <int BITS, int GS, int MT, int KS, int D>
 __global__ __launch_bounds__(512) void w4a16_stream_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, const int32_t *__restrict__ qweight,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ldy, int M, int N, int K, int S,
     int tiles, float *__restrict__ part, size_t part_bytes, int *__restrict__ cnt) {
-    using SG = W4Stage<BITS, GS, MT>;
+    using SG = W4Stage<BITS, GS, MT, KS>;
     constexpr int RING = D * SG::BYTES;
     // One LDS object only (see the W8A8 decode kernel); the split flag sits after the ring.
     __shared__ __attribute__((aligned(1024))) char lds[RING + 16];
@@ -175,7 +186,7 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
     const int m0 = blockIdx.y * SG::ROWS;
     const int mrows = min(M - m0, SG::ROWS);
     const int n0 = t * kTN;
-    const int G = K >> 7;
+    const int G = K / SG::KPS;  // stages
     const int g0 = (int)((int64_t)s * G / S), g1 = (int)((int64_t)(s + 1) * G / S);
     const int ng = g1 - g0;
 
@@ -206,13 +217,14 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
         const int piece = sl ^ w4_swz<BITS>(r);
         w_voff[j] = (int)(((uint32_t)r * (uint32_t)N + (uint32_t)min(n0 + 4 * piece, N - 4)) * 4u);
     }
-    // Activations: copy c fills rows 4c .. 4c+3 (16 pieces each); rows past the chunk
-    // repeat its last row (never stored).
+    // Activations: copy c fills rows RPC*c .. RPC*c + RPC-1 (64/RPC pieces each); rows
+    // past the chunk repeat its last row (never stored).
+    constexpr int LPR = 64 / SG::RPC;  // lanes (16-byte pieces) per activation row
     int a_voff[SG::AI], a_ins[SG::AI];
 #pragma unroll
     for (int j = 0; j < SG::AI; ++j) {
         a_ins[j] = min(wave * SG::AI + j, SG::ACOPIES - 1);
-        const int row = 4 * a_ins[j] + (lane >> 4), sl = lane & 15;
+        const int row = SG::RPC * a_ins[j] + lane / LPR, sl = lane % LPR;
         const int piece = sl ^ (row & 15);
         a_voff[j] = (int)(((uint32_t)min(row, mrows - 1) * (uint32_t)ldx + (uint32_t)piece * 8u) * 2u);
     }
@@ -220,7 +232,7 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
 #pragma unroll
     for (int j = 0; j < SG::AI; ++j) {
         a_insp[j] = min((wave + 4) * SG::AI + j, SG::ACOPIES - 1);
-        const int row = 4 * a_insp[j] + (lane >> 4), sl = lane & 15;
+        const int row = SG::RPC * a_insp[j] + lane / LPR, sl = lane % LPR;
         const int piece = sl ^ (row & 15);
         a_voffp[j] = (int)(((uint32_t)min(row, mrows - 1) * (uint32_t)ldx + (uint32_t)piece * 8u) * 2u);
     }
@@ -239,18 +251,19 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
 #pragma unroll
     for (int k = 0; k < D - 1; ++k)
         if (k < ng && wave < 4) {
-            w4_issue<BITS, GS, MT>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, sr, w_voff, a_voff, a_ins, s_half,
-                                   s_voff);
-            w4_issue_partner<BITS, GS, MT>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, w_voff, a_voffp, a_insp);
+            w4_issue<BITS, GS, MT, KS>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, sr, w_voff, a_voff, a_ins,
+                                       s_half, s_voff);
+            w4_issue_partner<BITS, GS, MT, KS>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, w_voff, a_voffp,
+                                               a_insp);
         }
 
     // This lane's B words: column 16*wave + li of packed row 4*ks + lb (4 bits) or of
     // packed rows 8*ks + 2*lb and the next (8 bits): the K values 32*ks + 8*lb .. +7.
     const int cl = 16 * wave + li;
     constexpr int BW = BITS == 4 ? 1 : 2;
-    int b_off[4][BW];
+    int b_off[KS][BW];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int e = 0; e < BW; ++e) {
             const int r = BITS == 4 ? 4 * ks + lb : 8 * ks + 2 * lb + e;
@@ -265,21 +278,22 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
         __builtin_amdgcn_sched_barrier(0);
         if (u + D - 1 < ng && wave < 4) {
             char *const nst = lds + (slot == 0 ? D - 1 : slot - 1) * SG::BYTES;
-            w4_issue<BITS, GS, MT>(nst, g0 + u + D - 1, wave, N, wr, xr, sr, w_voff, a_voff, a_ins, s_half, s_voff);
-            w4_issue_partner<BITS, GS, MT>(nst, g0 + u + D - 1, wave, N, wr, xr, w_voff, a_voffp, a_insp);
+            w4_issue<BITS, GS, MT, KS>(nst, g0 + u + D - 1, wave, N, wr, xr, sr, w_voff, a_voff, a_ins, s_half,
+                                       s_voff);
+            w4_issue_partner<BITS, GS, MT, KS>(nst, g0 + u + D - 1, wave, N, wr, xr, w_voff, a_voffp, a_insp);
         }
         __builtin_amdgcn_sched_barrier(0);
         const char *st = lds + slot * SG::BYTES;
-        // The group's four words are dequantised first, at raised wave priority: with
+        // The stage's KS words are dequantised first, at raised wave priority: with
         // the two waves of a SIMD both holding VALU work, the dequantisation goes first
         // and the MFMAs that need it start sooner (measured 2-6% faster on the decode
         // layers at M = 8 and 64, except qkv at M = 8, 2% slower).
-        v8bf bw[4];
+        v8bf bw[KS];
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             if constexpr (BITS == 4)
                 bw[ks] = dequant8x16((uint32_t)*reinterpret_cast<const int *>(st + b_off[ks][0]));
             else
@@ -291,32 +305,28 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
         __builtin_amdgcn_sched_barrier(0);
         v4f p[MT];
         const float *const srow = reinterpret_cast<const float *>(st + SG::WB + SG::AB);
+        constexpr int KSG = GS / 32;  // K steps per group
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             const v8bf b = bw[ks];
-            // group 32: every K step is a group of its own (a fresh sum, folded below)
-            const bool fresh = ks == 0 || SG::NSG == 4;
+            // a group's first K step starts a fresh sum
+            const bool fresh = ks % KSG == 0;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int row = mt * 16 + li;
-                const v4i a = *reinterpret_cast<const v4i *>(st + SG::WB + row * 256 + (((4 * ks + lb) ^ li) << 4));
+                const v4i a =
+                    *reinterpret_cast<const v4i *>(st + SG::WB + row * SG::ROWB + (((4 * ks + lb) ^ li) << 4));
                 p[mt] = mfma_bf16(a, b, fresh ? v4f{0.f, 0.f, 0.f, 0.f} : p[mt]);
             }
-            if constexpr (SG::NSG == 4) {
-                const float sc = srow[ks * kTN + cl];
+            if (ks % KSG == KSG - 1) {
+                // the group's sum, scaled (4 bits: the sums are of 16*q, the scale takes the
+                // 1/16, exact)
+                const float sc = srow[(ks / KSG) * kTN + cl] * (BITS == 4 ? 0.0625f : 1.0f);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) acc[mt][r] += sc * p[mt][r];
             }
-        }
-        if constexpr (SG::NSG == 1) {
-            // 4 bits: the sums are of 16*q, the scale takes the 1/16 (exact)
-            const float sc = srow[cl] * (BITS == 4 ? 0.0625f : 1.0f);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[mt][r] += sc * p[mt][r];
         }
         slot = slot == D - 1 ? 0 : slot + 1;
     }
@@ -389,13 +399,12 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
 }
 
 struct W4Plan {
-    int MT, S, tiles, blocks, chunks;
+    int MT, KS, S, tiles, blocks, chunks;
 };
 
-W4Plan w4_plan(int M, int N, int K) {
+W4Plan w4_plan(int M, int N, int K, int bits) {
     W4Plan p;
     p.tiles = (N + kTN - 1) / kTN;
-    const int G = K / kGroup;
     // Target 1.5 workgroups per CU: two fit on a CU (LDS), and the second one's waves
     // hide the first one's dequantisation and barrier latencies (measured best of 1, 1.5, 2).
     // Layers with more tiles than CUs take 3 per CU (gate_up: 34.5 -> 31.8 us at M = 8).
@@ -403,6 +412,10 @@ W4Plan w4_plan(int M, int N, int K) {
     const int P = p.tiles > cus ? 3 * cus : 3 * cus / 2;
     auto plan = [&](int mt) {
         p.MT = mt;
+        // 4 bits with one 16-row m tile: two groups per stage (the stage then carries as
+        // many weight bytes as an 8-bit one, and the per-stage hand-off is paid half as often)
+        p.KS = bits == 4 && mt == 1 && K % 256 == 0 ? 8 : 4;
+        const int G = K / (32 * p.KS);  // stages
         p.chunks = (M + 16 * mt - 1) / (16 * mt);
         int S = (P + p.tiles * p.chunks - 1) / (p.tiles * p.chunks);
         if (S > G) S = G;
@@ -414,47 +427,55 @@ W4Plan w4_plan(int M, int N, int K) {
     // Narrow layers at M > 32: when the splits would leave a workgroup fewer than 8 groups,
     // chunks of 32 rows (twice the workgroups per tile, half the splits) are faster
     // (measured at M = 64: qkv 20.2 -> 18.1 us, o_proj 20.3 -> 15.9 us; wide layers lose).
-    if (p.MT > 2 && G < 8 * p.S) plan(2);
+    if (p.MT > 2 && K / kGroup < 8 * p.S) plan(2);
     p.blocks = ((p.tiles * p.S + 7) / 8) * 8;
     return p;
 }
 
 // As many stages as fit in 80 KiB (two workgroups per CU), at most 6.
-template <int BITS, int GS, int MT>
+template <int BITS, int GS, int MT, int KS>
 hipError_t launch_w4_mt(const W4A16Args &a, const W4Plan &p, hipStream_t st) {
-    constexpr int FIT = (80 * 1024 - 16) / W4Stage<BITS, GS, MT>::BYTES;
+    constexpr int FIT = (80 * 1024 - 16) / W4Stage<BITS, GS, MT, KS>::BYTES;
     constexpr int D = FIT < 6 ? FIT : 6;
     static_assert(D >= 2, "at least two stages");
     int *cnt = p.S > 1 ? a.counters : nullptr;
     float *part = p.S > 1 ? (float *)a.ws : nullptr;
     dim3 grid(p.blocks, p.chunks);
-    w4a16_stream_kernel<BITS, GS, MT, D><<<grid, 512, 0, st>>>(a.x, a.ldx, a.qweight, a.w_scale, a.y, a.ldy, a.M,
-                                                              a.N, a.K, p.S, p.tiles, part,
-                                                              p.S > 1 ? a.ws_bytes : 0, cnt);
+    w4a16_stream_kernel<BITS, GS, MT, KS, D><<<grid, 512, 0, st>>>(a.x, a.ldx, a.qweight, a.w_scale, a.y, a.ldy,
+                                                                  a.M, a.N, a.K, p.S, p.tiles, part,
+                                                                  p.S > 1 ? a.ws_bytes : 0, cnt);
     return hipGetLastError();
 }
 
 template <int BITS, int GS>
 hipError_t launch_w4_bits(const W4A16Args &a, const W4Plan &p, hipStream_t s) {
     switch (p.MT) {
-        case 1: return launch_w4_mt<BITS, GS, 1>(a, p, s);
-        case 2: return launch_w4_mt<BITS, GS, 2>(a, p, s);
-        case 3: return launch_w4_mt<BITS, GS, 3>(a, p, s);
-        default: return launch_w4_mt<BITS, GS, 4>(a, p, s);
+        case 1:
+            if constexpr (BITS == 4)
+                if (p.KS == 8) return launch_w4_mt<BITS, GS, 1, 8>(a, p, s);
+            return launch_w4_mt<BITS, GS, 1, 4>(a, p, s);
+        case 2: return launch_w4_mt<BITS, GS, 2, 4>(a, p, s);
+        case 3: return launch_w4_mt<BITS, GS, 3, 4>(a, p, s);
+        default: return launch_w4_mt<BITS, GS, 4, 4>(a, p, s);
     }
 }
 
 }  // namespace
 
 // Partial-sum bytes after the counter region (0 when K is not split).
+// Enough for either code width (the 4-bit plan splits K at most as often as the 8-bit one).
 size_t w4a16_gemm_workspace(int M, int N, int K) {
-    const W4Plan p = w4_plan(M, N, K);
-    if (p.S <= 1) return 0;
-    return align256(size_t(p.tiles) * p.chunks * p.S * 8 * p.MT * 4 * 64 * sizeof(float));
+    size_t bytes = 0;
+    for (const int bits : {4, 8}) {
+        const W4Plan p = w4_plan(M, N, K, bits);
+        if (p.S > 1)
+            bytes = std::max(bytes, align256(size_t(p.tiles) * p.chunks * p.S * 8 * p.MT * 4 * 64 * sizeof(float)));
+    }
+    return bytes;
 }
 
 hipError_t launch_w4a16_gemm(const W4A16Args &a, hipStream_t s) {
-    const W4Plan p = w4_plan(a.M, a.N, a.K);
+    const W4Plan p = w4_plan(a.M, a.N, a.K, a.bits);
     if (a.bits == 8) return a.group == 32 ? launch_w4_bits<8, 32>(a, p, s) : launch_w4_bits<8, 128>(a, p, s);
     return launch_w4_bits<4, 128>(a, p, s);
 }

@@ -31,7 +31,8 @@ def test_w4a16_decode_layer(layer, M):
     assert beyond <= max(1, y_exact.size // 10_000), (beyond, maxulp)
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 128, 8), (8, 512, 256), (13, 384, 40), (65, 256, 136), (130, 640, 264)])
+@pytest.mark.parametrize("M,K,N", [(1, 128, 8), (8, 512, 256), (13, 384, 40), (13, 768, 40), (16, 2816, 264),
+                                   (65, 256, 136), (130, 640, 264)])
 def test_w4a16_ragged(M, K, N):
     xb = synth.activations_bf16(1, f"w4r{M}-{K}-{N}", M, K, outliers=True)
     words = synth.uniform_words(1, f"w4rw{M}-{K}-{N}", (K // 8) * N).reshape(K // 8, N)  # all 16 nibble values
@@ -52,7 +53,7 @@ def test_w4a16_repeatable():
     assert np.array_equal(host_bf16_bits(a), host_bf16_bits(b))
 
 
-@pytest.mark.parametrize("M,K,N", [(8, 640, 264), (64, 1280, 392), (70, 384, 136)])
+@pytest.mark.parametrize("M,K,N", [(8, 640, 264), (8, 1280, 264), (64, 1280, 392), (70, 384, 136)])
 def test_w4a16_strided_rows(M, K, N):
     """x and y addressed with row strides larger than K and N (ldx = K + 64, ldy = N + 24):
     the padding columns of y stay untouched."""

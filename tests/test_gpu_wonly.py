@@ -44,8 +44,8 @@ def test_decode_layer(layer, M, bits, group):
 
 
 @pytest.mark.parametrize("bits,group", SCHEMES)
-@pytest.mark.parametrize("M,K,N", [(1, 128, 8), (13, 384, 40), (16, 640, 264), (17, 256, 520), (33, 1152, 136),
-                                   (64, 384, 1032), (65, 640, 264), (130, 1024, 72)])
+@pytest.mark.parametrize("M,K,N", [(1, 128, 8), (13, 384, 40), (16, 640, 264), (16, 1024, 264), (17, 256, 520),
+                                   (33, 1152, 136), (64, 384, 1032), (65, 640, 264), (130, 1024, 72)])
 def test_ragged(M, K, N, bits, group):
     """Uniformly random codes (every code value) and positive scales; K with a half last
     chunk (384, 640, 1152), N not a multiple of the 256-column tile, M across the 16-row tiles
