@@ -476,8 +476,12 @@ def main():
                 torch.cuda.synchronize()
                 gm, _, _ = timer.mean_us(("w4", L.name, Mw))
                 b = w4_bytes(Mw, L.K, L.N)
+                # bf16 MFMA work: 2*M*N*K useful flops (the 16-row tiles pad M = 8 to 16)
+                tfl = 2.0 * Mw * L.N * L.K / (gm * 1e-6) / 1e12
                 w4[f"{L.name}_M{Mw}"] = {"us": round(gm, 3), "GBps": round(b / (gm * 1e-6) / 1e9, 1),
-                                         "frac_hbm": round(b / (gm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                                         "frac_hbm": round(b / (gm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                         "bf16_TFLOPS": round(tfl, 1),
+                                         "frac_bf16_peak": round(tfl / BF16_PEAK_TFLOPS, 4)}
             del copies, qw, sc
             torch.cuda.empty_cache()
         out["w4a16"] = w4
