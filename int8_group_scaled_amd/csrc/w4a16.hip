@@ -26,14 +26,15 @@
 // and two consecutive words at 8 bits.
 //
 // Data flow (as in the W8A8 decode kernel): a workgroup of 8 waves owns a tile of
-// 128 columns (16 per wave) and up to 64 rows, and walks its K groups through a
-// D-stage LDS ring filled by buffer_load ... lds copies -- a stage holds the group's
-// 16 (4 bits) or 32 (8 bits) packed weight rows of the tile, its activation rows (bf16,
-// 256 bytes each) and the tile's scales -- with the wait for a stage issued D - 2 stages behind the
-// copies, so D - 1 groups are in flight.  K is split across S workgroups when the
-// column tiles alone cannot fill the GPU; the splits publish fp32 partials with
-// device-coherent stores and the last to arrive sums them in split order.  Rows
-// are processed in chunks of 64 (gridDim.y).
+// 128 columns (16 per wave) and up to 64 rows, and walks its K range through a
+// D-stage LDS ring filled by buffer_load ... lds copies -- a stage holds one group's
+// 16 (4 bits) or 32 (8 bits) packed weight rows of the tile (two groups, 32 rows, at
+// 4 bits with one 16-row m tile), its activation rows (bf16) and the tile's scales --
+// with the wait for a stage issued D - 2 stages behind the copies, so D - 1 stages are
+// in flight.  K is split across S workgroups when the column tiles alone cannot fill
+// the GPU; the splits publish fp32 partials with device-coherent stores and the last
+// to arrive sums them in split order.  Rows are processed in chunks of up to 64
+// (gridDim.y).
 #include <algorithm>
 
 #include "internal.h"
