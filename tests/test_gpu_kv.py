@@ -81,6 +81,7 @@ def _qk_case(Mq, T, Hq, Hkv, seed, scale=128 ** -0.5):
 
 @pytest.mark.parametrize("Mq,T,Hq,Hkv", [(8, 2048, 32, 8), (3, 77, 4, 1), (17, 129, 2, 2), (1, 1, 1, 1),
                                          (64, 300, 8, 8), (8, 16384, 32, 8),
+                                         (8, 4100, 32, 8),     # two waves per workgroup, ragged last block
                                          (8, 32768, 32, 8),    # the benchmark's long context
                                          (40, 161, 8, 2),      # 160 rows per KV head: three row blocks
                                          (3, 200, 32, 1),      # one KV head shared by 32 query heads
