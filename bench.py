@@ -28,7 +28,9 @@ GEMM kernel on pre-quantised activations) in TOP/s against the 5.0 POP/s dense I
 peak; the INT8 vocabulary head (64 tokens x 248320 columns); the weight-only GEMMs
 (W4A16 g128 and W8A16 g128 / g32 on the decode shapes at 8 and 64 tokens, and the
 INT4 / INT8 weight-only vocabulary heads at 1, 8 and 64 tokens); the RMS
-normalisation fused with the quantisation; the achievable peaks measured in the same
+normalisation fused with the quantisation; one GPU's share at tensor-parallel size 4
+(qkv and gate/up by columns, o_proj and down by K, a quarter of the vocabulary head;
+decode and prefill GEMM); the achievable peaks measured in the same
 run (a streaming-read kernel and an INT8 MFMA loop, libi8gs_peaks.so); clocks and
 software versions; and the CPU oracle on the host cores (the decode step, per layer,
 and single-threaded on the single linear and qkv).
@@ -603,6 +605,40 @@ def main():
         del w, qw, sc, x64, qa, s, y
         torch.cuda.empty_cache()
         log(f"vocabulary heads: " + ", ".join(f"{k} {v['GBps']:.0f} GB/s" for k, v in heads.items()))
+
+    if not args.no_extras:
+        # ---------------- one GPU's share at tensor-parallel size 4: the decode (64 tokens) and
+        # prefill (4096 tokens) GEMM on the shard shapes, pre-quantised activations, cold weights
+        shards = {}
+        for L in synth.SHARD_LAYERS + (synth.LAYERS["lm_head_tp4"],):
+            w = torch.from_numpy(synth.weights_f32(0, f"bench-tp4-{L.name}", L.K, L.N)).to(dev)
+            qw, sc = i8.gptq_quantize_rtn(w, 8)
+            del w
+            copies = cold_copies((qw, sc), qw.numel() * 4)
+            e = {"K": L.K, "N": L.N}
+            for Ms in ((64,) if L.name == "lm_head_tp4" else (64, 4096)):
+                xb = synth.activations_bf16(0, f"bench-tp4-{L.name}-{Ms}", Ms, L.K, outliers=True)
+                x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+                qa, s = i8.quant_act_per_token(x)
+                y = torch.empty((Ms, L.N), dtype=torch.bfloat16, device=dev)
+                calls = [lambda c=c: i8.gemm_w8a8_g128(c[0], c[1], qa=qa, a_scale=s, y=y) for c in copies]
+                gm = timed(("tp4", L.name, Ms), calls, 50 if Ms == 64 else 10)
+                if Ms == 64:
+                    b = gemm_bytes(Ms, L.K, L.N)
+                    e.update(decode_us=round(gm, 3), decode_GBps=round(b / (gm * 1e-6) / 1e9, 1),
+                             decode_frac_hbm=round(b / (gm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+                else:
+                    tops = 2.0 * Ms * L.N * L.K / (gm * 1e-6) / 1e12
+                    e.update(prefill_us=round(gm, 2), prefill_TOPS=round(tops, 1),
+                             prefill_frac_int8_peak=round(tops / INT8_PEAK_TOPS, 4))
+                del x, qa, s, y, calls
+            shards[L.name] = e
+            del copies, qw, sc
+            torch.cuda.empty_cache()
+        out["tp4_shard"] = shards
+        log("tensor-parallel-4 shards: " + ", ".join(
+            f"{k} {v['decode_GBps']:.0f} GB/s" + (f" / {v['prefill_TOPS']:.0f} TOP/s" if "prefill_TOPS" in v else "")
+            for k, v in shards.items()))
 
     # ---------------- measured ceilings and environment
     peaks = measured_peaks(torch, dev)

@@ -16,4 +16,4 @@ from .gen import (  # noqa: F401
     weights_f32,
     sample_rows,
 )
-from .workloads import LAYERS, DECODE_LAYERS, PREFILL_LAYERS, Layer, config  # noqa: F401
+from .workloads import LAYERS, DECODE_LAYERS, PREFILL_LAYERS, SHARD_LAYERS, Layer, config  # noqa: F401

@@ -39,7 +39,21 @@ SINGLE = Layer("single", 512, 256)
 
 DECODE_LAYERS = (QKV, O_PROJ, GATE_UP, DOWN)
 PREFILL_LAYERS = (QKV, O_PROJ, GATE_UP, DOWN, FC)
-LAYERS = {l.name: l for l in (QKV, O_PROJ, GATE_UP, DOWN, FC, LM_HEAD, SINGLE)}
+
+# One GPU's share under the tensor-parallel size 4 both serving recipes fix (Flint card,
+# serving recipe; target model card, serving section): the column-parallel layers (qkv,
+# gate/up, vocabulary head) keep K and take N/4 output columns; the row-parallel ones
+# (o_proj, down) keep N and take K/4, on 128-wide group boundaries (8 and 34 groups).
+TP = 4
+QKV_TP = Layer("qkv_tp4", HIDDEN, (Q_HEADS + 2 * KV_HEADS) * HEAD_DIM // TP)
+O_PROJ_TP = Layer("o_proj_tp4", Q_HEADS * HEAD_DIM // TP, HIDDEN)
+GATE_UP_TP = Layer("gate_up_tp4", HIDDEN, 2 * INTERMEDIATE // TP)
+DOWN_TP = Layer("down_tp4", INTERMEDIATE // TP, HIDDEN)
+LM_HEAD_TP = Layer("lm_head_tp4", HIDDEN, VOCAB // TP)
+SHARD_LAYERS = (QKV_TP, O_PROJ_TP, GATE_UP_TP, DOWN_TP)
+
+LAYERS = {l.name: l for l in (QKV, O_PROJ, GATE_UP, DOWN, FC, LM_HEAD, SINGLE, QKV_TP, O_PROJ_TP, GATE_UP_TP,
+                              DOWN_TP, LM_HEAD_TP)}
 
 
 def config(name: str) -> dict:

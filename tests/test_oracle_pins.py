@@ -377,3 +377,19 @@ def test_drafter_shapes_fixture():
     other = kv["params_total_billion"] * 1e9 - quantised
     int4_bytes = quantised / 2 + quantised / 128 * 2 + other * 2
     assert abs(int4_bytes / 1e9 - kv["quantized_gb"]) / kv["quantized_gb"] < 0.05
+
+
+def test_tp4_shard_shapes():
+    """One GPU's share at tensor-parallel size 4: four column shards (qkv, gate/up, vocabulary
+    head) or four row shards (o_proj, down) rebuild the full layer, and every shard keeps
+    whole 128-wide groups and a column count the kernels accept."""
+    L = synth.LAYERS
+    for full, shard, axis in (("qkv", "qkv_tp4", "N"), ("gate_up", "gate_up_tp4", "N"), ("lm_head", "lm_head_tp4", "N"),
+                              ("o_proj", "o_proj_tp4", "K"), ("down", "down_tp4", "K")):
+        f, s = L[full], L[shard]
+        other = "K" if axis == "N" else "N"
+        assert getattr(s, axis) * 4 == getattr(f, axis) and getattr(s, other) == getattr(f, other)
+        assert s.K % 128 == 0 and s.N % 8 == 0
+    # the row shards cut K on group boundaries: 8 and 34 groups per GPU
+    assert L["o_proj_tp4"].K // 128 == 8 and L["down_tp4"].K // 128 == 34
+    assert synth.SHARD_LAYERS == tuple(L[n] for n in ("qkv_tp4", "o_proj_tp4", "gate_up_tp4", "down_tp4"))
