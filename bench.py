@@ -61,8 +61,8 @@ HBM_PEAK_GBS = 8000.0
 # is reported as null.
 DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h")
 DECODE_TRAFFIC = {
-    "sources_sha256": "3f2706a24a67c1d57b433f24187ab53086f3515c88c665dc65d9abdc7bb4f0f0",
-    "fetch": {"qkv": 36819660, "o_proj": 26534833, "gate_up": 189721794, "down": 107572700},
+    "sources_sha256": "d3b618cf7f4a0112985719949892d5286c5ae44c202016281d3b97f9411d61d5",
+    "fetch": {"qkv": 36819492, "o_proj": 26534897, "gate_up": 190052384, "down": 107573052},
     "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456448, "down": 8528640},
 }
 EVENT_EVERY = 8  # per-kernel HIP events on every 8th timed step (each event adds a gap)
