@@ -286,16 +286,18 @@ __global__ __launch_bounds__(256) void attn_pv_reduce_kernel(const float *__rest
     const int SG = (S + 3) / 4;
     const int s0 = g * SG, s1 = min(S, s0 + SG);
     const float *src = part + (int64_t)tile * S * 4096 + c;
+    // Up to 16 splits' cells in flight at once, then added in split order: the loads are
+    // unconditional (an index past this group's last split reads that split again) so
+    // that none waits for the one before it.
     float sum = 0.0f;
-    int sp = s0;
-    for (; sp + 8 <= s1; sp += 8) {
-        float v[8];
+    for (int c0 = s0; c0 < s1; c0 += 16) {
+        float v[16];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = src[(int64_t)(sp + k) * 4096];
+        for (int k = 0; k < 16; ++k) v[k] = src[(int64_t)min(c0 + k, s1 - 1) * 4096];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sum += v[k];
+        for (int k = 0; k < 16; ++k)
+            if (c0 + k < s1) sum += v[k];
     }
-    for (; sp < s1; ++sp) sum += src[(int64_t)sp * 4096];
     s_sum[g][threadIdx.x & 63] = sum;
     __syncthreads();
     if (g == 0) {
