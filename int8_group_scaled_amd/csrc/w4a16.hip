@@ -70,7 +70,11 @@ __device__ __forceinline__ v4f mfma_bf16(v4i a, v8bf b, v4f c) {
 // read's four lane groups read rows that land in different banks); then the activation
 // rows, 2 * 32 * KS bytes each, pieces permuted by XOR with row % 16; then the 128 scales
 // of each of the stage's scale rows.
-template <int BITS, int GS, int MT, int KS = 4>
+//
+// TAG (the kernel's ring depth) only gives each kernel instantiation shape types of its
+// own: a device function template taking buffer resources, used with one shape from two
+// kernel instantiations, fails overload resolution in hipcc's host pass.
+template <int BITS, int GS, int MT, int KS = 4, int TAG = 0>
 struct W4Stage {
     static_assert((BITS == 4 && GS == 128 && (KS == 4 || KS == 8)) ||
                       (BITS == 8 && (GS == 128 || GS == 32) && KS == 4),
@@ -102,13 +106,13 @@ __device__ __forceinline__ int w4_swz(int r) {
 // 2*(WPW*wave + j) and the next), its activation copies and its scale copies (one scale
 // row: half wave % 2 of the tile's 128 scales; several: both halves of scale row
 // wave % NSG).
-template <int BITS, int GS, int MT, int KS>
+template <int BITS, int GS, int MT, int KS, int TAG>
 __device__ __forceinline__ void w4_issue(char *st, int g, int wave, int N, __amdgpu_buffer_rsrc_t wr,
                                          __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t sr,
-                                         const int (&w_voff)[W4Stage<BITS, GS, MT, KS>::WPW],
-                                         const int (&a_voff)[W4Stage<BITS, GS, MT, KS>::AI],
-                                         const int (&a_ins)[W4Stage<BITS, GS, MT, KS>::AI], int s_half, int s_voff) {
-    using SG = W4Stage<BITS, GS, MT, KS>;
+                                         const int (&w_voff)[W4Stage<BITS, GS, MT, KS, TAG>::WPW],
+                                         const int (&a_voff)[W4Stage<BITS, GS, MT, KS, TAG>::AI],
+                                         const int (&a_ins)[W4Stage<BITS, GS, MT, KS, TAG>::AI], int s_half, int s_voff) {
+    using SG = W4Stage<BITS, GS, MT, KS, TAG>;
 #pragma unroll
     for (int j = 0; j < SG::WPW; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, I8GS_LDS(st + (wave * SG::WPW + j) * 1024), 16, w_voff[j],
@@ -135,13 +139,13 @@ __device__ __forceinline__ void w4_issue(char *st, int g, int wave, int N, __amd
 // The copies of wave + 4's share, issued by wave (0-3) too: its weight rows lie 8*WPW
 // further down, its activation copies are given by a_voff / a_ins (its scales repeat
 // those of this wave, or are copied by waves 0-3 themselves, and are not copied again).
-template <int BITS, int GS, int MT, int KS>
+template <int BITS, int GS, int MT, int KS, int TAG>
 __device__ __forceinline__ void w4_issue_partner(char *st, int g, int wave, int N, __amdgpu_buffer_rsrc_t wr,
                                                  __amdgpu_buffer_rsrc_t xr,
-                                                 const int (&w_voff)[W4Stage<BITS, GS, MT, KS>::WPW],
-                                                 const int (&a_voff)[W4Stage<BITS, GS, MT, KS>::AI],
-                                                 const int (&a_ins)[W4Stage<BITS, GS, MT, KS>::AI]) {
-    using SG = W4Stage<BITS, GS, MT, KS>;
+                                                 const int (&w_voff)[W4Stage<BITS, GS, MT, KS, TAG>::WPW],
+                                                 const int (&a_voff)[W4Stage<BITS, GS, MT, KS, TAG>::AI],
+                                                 const int (&a_ins)[W4Stage<BITS, GS, MT, KS, TAG>::AI]) {
+    using SG = W4Stage<BITS, GS, MT, KS, TAG>;
 #pragma unroll
     for (int j = 0; j < SG::WPW; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, const int32_t *__restrict__ qweight,
     const float *__restrict__ w_scale, uint16_t *__restrict__ y, int64_t ldy, int M, int N, int K, int S,
     int tiles, float *__restrict__ part, size_t part_bytes, int *__restrict__ cnt) {
-    using SG = W4Stage<BITS, GS, MT, KS>;
+    using SG = W4Stage<BITS, GS, MT, KS, D>;
     constexpr int RING = D * SG::BYTES;
     // One LDS object only (see the W8A8 decode kernel); the split flag sits after the ring.
     __shared__ __attribute__((aligned(1024))) char lds[RING + 16];
@@ -252,9 +256,9 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
 #pragma unroll
     for (int k = 0; k < D - 1; ++k)
         if (k < ng && wave < 4) {
-            w4_issue<BITS, GS, MT, KS>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, sr, w_voff, a_voff, a_ins,
+            w4_issue<BITS, GS, MT, KS, D>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, sr, w_voff, a_voff, a_ins,
                                        s_half, s_voff);
-            w4_issue_partner<BITS, GS, MT, KS>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, w_voff, a_voffp,
+            w4_issue_partner<BITS, GS, MT, KS, D>(lds + k * SG::BYTES, g0 + k, wave, N, wr, xr, w_voff, a_voffp,
                                                a_insp);
         }
 
@@ -279,9 +283,9 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
         __builtin_amdgcn_sched_barrier(0);
         if (u + D - 1 < ng && wave < 4) {
             char *const nst = lds + (slot == 0 ? D - 1 : slot - 1) * SG::BYTES;
-            w4_issue<BITS, GS, MT, KS>(nst, g0 + u + D - 1, wave, N, wr, xr, sr, w_voff, a_voff, a_ins, s_half,
+            w4_issue<BITS, GS, MT, KS, D>(nst, g0 + u + D - 1, wave, N, wr, xr, sr, w_voff, a_voff, a_ins, s_half,
                                        s_voff);
-            w4_issue_partner<BITS, GS, MT, KS>(nst, g0 + u + D - 1, wave, N, wr, xr, w_voff, a_voffp, a_insp);
+            w4_issue_partner<BITS, GS, MT, KS, D>(nst, g0 + u + D - 1, wave, N, wr, xr, w_voff, a_voffp, a_insp);
         }
         __builtin_amdgcn_sched_barrier(0);
         const char *st = lds + slot * SG::BYTES;
@@ -401,6 +405,7 @@ __global__ __launch_bounds__(512) void w4a16_stream_kernel(
 
 struct W4Plan {
     int MT, KS, S, tiles, blocks, chunks;
+    bool one_per_cu;  // the CU's whole LDS is this workgroup's
 };
 
 W4Plan w4_plan(int M, int N, int K, int bits) {
@@ -423,7 +428,8 @@ W4Plan w4_plan(int M, int N, int K, int bits) {
         const int G = K / (32 * p.KS);  // stages
         p.chunks = (M + 16 * mt - 1) / (16 * mt);
         const int units = p.tiles * p.chunks;
-        int S = 2 * units <= cus ? cus / units : (P + units - 1) / units;
+        p.one_per_cu = 2 * units <= cus;
+        int S = p.one_per_cu ? cus / units : (P + units - 1) / units;
         if (S > G) S = G;
         if (S < 1) S = 1;
         if (units > kMaxCounters) S = 1;
@@ -438,10 +444,10 @@ W4Plan w4_plan(int M, int N, int K, int bits) {
     return p;
 }
 
-// As many stages as fit in 80 KiB (two workgroups per CU), at most 6.
-template <int BITS, int GS, int MT, int KS>
-hipError_t launch_w4_mt(const W4A16Args &a, const W4Plan &p, hipStream_t st) {
-    constexpr int FIT = (80 * 1024 - 16) / W4Stage<BITS, GS, MT, KS>::BYTES;
+// As many stages as fit in BUDGET KiB, at most 6.
+template <int BITS, int GS, int MT, int KS, int BUDGET>
+hipError_t launch_w4_ring(const W4A16Args &a, const W4Plan &p, hipStream_t st) {
+    constexpr int FIT = (BUDGET * 1024 - 16) / W4Stage<BITS, GS, MT, KS>::BYTES;
     constexpr int D = FIT < 6 ? FIT : 6;
     static_assert(D >= 2, "at least two stages");
     int *cnt = p.S > 1 ? a.counters : nullptr;
@@ -451,6 +457,18 @@ hipError_t launch_w4_mt(const W4A16Args &a, const W4Plan &p, hipStream_t st) {
                                                                   a.M, a.N, a.K, p.S, p.tiles, part,
                                                                   p.S > 1 ? a.ws_bytes : 0, cnt);
     return hipGetLastError();
+}
+
+// The ring takes 80 KiB, so that two workgroups share a CU, except where 80 KiB holds
+// only two stages (8-bit codes at 48 or 64 rows) and the workgroup has the CU to itself:
+// then the whole LDS (four stages at 64 rows: down at M = 64 38.5 -> 33.4 us, qkv
+// 19.9 -> 18.8 us; deeper rings where 80 KiB already holds three stages measured 5-12%
+// slower).
+template <int BITS, int GS, int MT, int KS>
+hipError_t launch_w4_mt(const W4A16Args &a, const W4Plan &p, hipStream_t st) {
+    if constexpr ((80 * 1024 - 16) / W4Stage<BITS, GS, MT, KS>::BYTES < 3)
+        if (p.one_per_cu) return launch_w4_ring<BITS, GS, MT, KS, 160>(a, p, st);
+    return launch_w4_ring<BITS, GS, MT, KS, 80>(a, p, st);
 }
 
 template <int BITS, int GS>
