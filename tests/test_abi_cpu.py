@@ -256,3 +256,51 @@ def test_kv_codec_and_attention_validation(lib):
     assert pv(A, A, A, 8, 32768, 32, 8, A, NUL, NUL, NUL, 0, NUL) == 4       # workspace missing
     assert pv(A, A, A, 8, 32768, 32, 8, A, NUL, NUL, A, need - 1, NUL) == 4  # workspace too small
     assert pv(A, A, A, 8, 32768, 32, 8, A, NUL, NUL, MIS, need, NUL) == 3    # workspace misaligned
+
+
+def test_decode_plan_on_tensor_parallel_shares(lib):
+    """Decode (M = 64) on one GPU's share at tensor-parallel size 4, read off the workspace
+    (without a GPU the CU count is taken as 256): where neither whole-fragment width keeps
+    its groups per split at the full grid, the K splits are capped -- 64-column tiles with
+    at least 8 groups per split (G/2 when K is shorter), else 128-column tiles with at least
+    16 -- and each split writes one fp32 piece of 64 rows x the chunk width."""
+    import int8_group_scaled_amd as i8
+    base = lambda K: 65536 + 64 * K + 256  # counters, then the quantised activations
+    piece = lambda tn: 64 * tn * 4
+    # qkv share (N = 1536, 40 groups): 24 tiles of 64 columns x 5 splits of 8 groups
+    # (the plain split would be 32 x 8 of 48 columns)
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 1536, 5120) == base(5120) + 24 * 5 * piece(64)
+    # o_proj share (K = 1024, 8 groups): 80 tiles of 64 columns x 2 splits of 4 groups
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 5120, 1024) == base(1024) + 80 * 2 * piece(64)
+    # gate/up share (N = 8704): no 64-column split fits; 68 tiles of 128 columns x 2 splits
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 8704, 5120) == base(5120) + 68 * 2 * piece(128)
+    # down share (K = 4352, 34 groups): the whole-fragment rule already applies, 80 x 3
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 5120, 4352) == base(4352) + 80 * 3 * piece(64)
+    # the four drafter layers keep their plans: qkv 96 x 2, o_proj 80 x 3, down 40 x 6 of
+    # 128 columns, gate_up unsplit
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 6144, 5120) == base(5120) + 96 * 2 * piece(64)
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 5120, 4096) == base(4096) + 80 * 3 * piece(64)
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 5120, 17408) == base(17408) + 40 * 6 * piece(128)
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 34816, 5120) == base(5120)
+
+
+def test_weight_only_plan_on_the_decode_layers(lib):
+    """The LDS-staged weight-only kernel's grid, read off the workspace (256 CUs without a
+    GPU): 128-column tiles x row chunks x K splits, one fp32 piece of 8 waves x MT*4 x 64
+    lanes per workgroup.  Narrow layers (tiles x chunks at most half the CUs) take one
+    workgroup per CU, floor(256 / (tiles * chunks)) splits; wider ones 1.5 per CU, or 3 per
+    CU with more tiles than CUs.  The workspace covers 4- and 8-bit codes alike."""
+    import int8_group_scaled_amd as i8
+    part = lambda units, S, MT: units * S * 8 * MT * 4 * 64 * 4
+    for op in (i8.OP_W4A16, i8.OP_WEIGHT_ONLY):
+        # M = 8 (one 16-row tile): qkv 48 tiles -> 5 splits; o_proj and down 40 tiles -> 6
+        assert i8.workspace_bytes(op, 8, 6144, 5120) == 65536 + part(48, 5, 1)
+        assert i8.workspace_bytes(op, 8, 5120, 4096) == 65536 + part(40, 6, 1)
+        assert i8.workspace_bytes(op, 8, 5120, 17408) == 65536 + part(40, 6, 1)
+        # gate_up: 272 tiles, more than the CUs -> 3 per CU: ceil(768 / 272) = 3 splits
+        assert i8.workspace_bytes(op, 8, 34816, 5120) == 65536 + part(272, 3, 1)
+        # M = 64: qkv and down keep 64-row tiles (5 and 6 splits); o_proj, whose 6 splits
+        # would leave 5 groups each, takes two 32-row chunks: 80 units -> 3 splits
+        assert i8.workspace_bytes(op, 64, 6144, 5120) == 65536 + part(48, 5, 4)
+        assert i8.workspace_bytes(op, 64, 5120, 17408) == 65536 + part(40, 6, 4)
+        assert i8.workspace_bytes(op, 64, 5120, 4096) == 65536 + part(80, 3, 2)
