@@ -461,7 +461,7 @@ hipError_t launch_w4_ring(const W4A16Args &a, const W4Plan &p, hipStream_t st) {
 
 // The ring takes 80 KiB, so that two workgroups share a CU, except where 80 KiB holds
 // only two stages (8-bit codes at 48 or 64 rows) and the workgroup has the CU to itself:
-// then the whole LDS (four stages at 64 rows: down at M = 64 38.5 -> 33.4 us, qkv
+// then the whole LDS (four stages at 64 rows: down at M = 64 38.2 -> 33.3 us, qkv
 // 19.9 -> 18.8 us; deeper rings where 80 KiB already holds three stages measured 5-12%
 // slower).
 template <int BITS, int GS, int MT, int KS>
