@@ -61,9 +61,9 @@ HBM_PEAK_GBS = 8000.0
 # is reported as null.
 DECODE_SOURCES = ("int8_group_scaled_amd/csrc/w8a8.hip", "int8_group_scaled_amd/csrc/internal.h")
 DECODE_TRAFFIC = {
-    "sources_sha256": "d3b618cf7f4a0112985719949892d5286c5ae44c202016281d3b97f9411d61d5",
-    "fetch": {"qkv": 36819492, "o_proj": 26534897, "gate_up": 190052384, "down": 107573052},
-    "write": {"qkv": 3941376, "o_proj": 4597760, "gate_up": 4456448, "down": 8528640},
+    "sources_sha256": "ac7e56bb4167989302daf04c9747fddf5fb48bb8008b8d7b4e504ace78d4b09d",
+    "fetch": {"qkv": 39961920, "o_proj": 26539296, "gate_up": 190730048, "down": 107590336},
+    "write": {"qkv": 7085568, "o_proj": 4597760, "gate_up": 4456448, "down": 8528640},
 }
 EVENT_EVERY = 8  # per-kernel HIP events on every 8th timed step (each event adds a gap)
 INT8_PEAK_TOPS = 5000.0

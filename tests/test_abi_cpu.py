@@ -276,9 +276,10 @@ def test_decode_plan_on_tensor_parallel_shares(lib):
     assert i8.workspace_bytes(i8.OP_W8A8, 64, 8704, 5120) == base(5120) + 68 * 2 * piece(128)
     # down share (K = 4352, 34 groups): the whole-fragment rule already applies, 80 x 3
     assert i8.workspace_bytes(i8.OP_W8A8, 64, 5120, 4352) == base(4352) + 80 * 3 * piece(64)
-    # the four drafter layers keep their plans: qkv 96 x 2, o_proj 80 x 3, down 40 x 6 of
-    # 128 columns, gate_up unsplit
-    assert i8.workspace_bytes(i8.OP_W8A8, 64, 6144, 5120) == base(5120) + 96 * 2 * piece(64)
+    # the four drafter layers: qkv 48 x 4 of 128 columns (10 groups per split: the rule for
+    # 128-column tiles with at least 4 splits filling three quarters of the grid), o_proj
+    # 80 x 3, down 40 x 6 of 128 columns, gate_up unsplit
+    assert i8.workspace_bytes(i8.OP_W8A8, 64, 6144, 5120) == base(5120) + 48 * 4 * piece(128)
     assert i8.workspace_bytes(i8.OP_W8A8, 64, 5120, 4096) == base(4096) + 80 * 3 * piece(64)
     assert i8.workspace_bytes(i8.OP_W8A8, 64, 5120, 17408) == base(17408) + 40 * 6 * piece(128)
     assert i8.workspace_bytes(i8.OP_W8A8, 64, 34816, 5120) == base(5120)

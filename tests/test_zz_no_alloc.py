@@ -36,7 +36,7 @@ def _check(M, K, N, tag, quantised=False):
 
 
 def test_noalloc_two_calls_second_smaller():
-    """A K-split decode layer (qkv: 96 tiles x 2 splits, fp32 pieces in the scratch array),
+    """A K-split decode layer (qkv: 48 tiles x 4 splits, fp32 pieces in the scratch array),
     then a smaller single linear: the second call reuses the array the first one left."""
     assert i8.noalloc_scratch_bytes() == 16 << 20
     _check(64, 5120, 6144, "na-qkv")
